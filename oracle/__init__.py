@@ -1,0 +1,14 @@
+"""CPU fp64 oracle for paged attention decode.
+
+TEST INFRASTRUCTURE: only tests/, the smoke check and the benchmark's CPU
+baseline leg may import this package. The GPU library never calls it.
+Every function here is pinned by tests against closed forms, brute force and
+a library routine; none is marked "parity unpinned".
+"""
+from .attention import (PAGE, attend_bruteforce, attend_online, attend_two_pass,
+                        bf16_to_f64, combine, gather_pages, scale_as_received,
+                        softmax_weights, visible_keys)
+
+__all__ = ["PAGE", "attend_bruteforce", "attend_online", "attend_two_pass",
+           "bf16_to_f64", "combine", "gather_pages", "scale_as_received",
+           "softmax_weights", "visible_keys"]
