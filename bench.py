@@ -1,0 +1,257 @@
+"""Benchmark of the paged MLA decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+One step is the whole path over one batch: the split-KV plan, the fused
+decode kernel and the split merge (mla_decode_plan + mla_decode, or
+gqa_decode for config 5), with inputs already resident in HBM. The default
+workload is the DeepSeek-V3-shaped decode: batch 64, one query token, 128
+heads, 576/512 head dims, every sequence 4096 tokens in 64-token pages.
+Three independent input sets rotate between steps so the 256 MB Infinity
+Cache cannot hold the working set.
+
+Prints one JSON line: decode tokens/s (value), TFLOP/s and HBM GB/s against
+MI355X peaks, the roofline of the dominant (decode) kernel timed by HIP
+events on its stream, and the CPU oracle's rate on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode TFLOPS + HBM GB/s (% MI355X peak); decode tokens/s at B=64"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16: 256 CU x 2.4 GHz x 4096 flop/clk
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "mla_paged_kv_03_amd", "csrc", "decode_kernels.hip")
+
+
+def algorithmic_work(d):
+    """Bytes and FLOPs an IO-optimal decode must move and compute: every
+    valid cached token once, q, out and lse; 2 (d_qk + d_v) flop per
+    (query row, visible key) pair."""
+    cfg = d["cfg"]
+    L = d["cache_seqlens"].astype(np.int64)
+    tok_bytes = cfg.h_kv * (cfg.d_qk * 2 if cfg.kind == "mla" else (cfg.d_qk + cfg.d_v) * 2)
+    rows = cfg.batch * cfg.s_q * cfg.h_q
+    kv = int(L.sum()) * tok_bytes
+    qb = rows * cfg.d_qk * 2
+    ob = rows * cfg.d_v * 2 + rows * 4
+    pairs = 0
+    for t in range(cfg.s_q):
+        vis = np.clip(L - cfg.s_q + 1 + t, 0, L) if cfg.causal else L
+        pairs += int(vis.sum()) * cfg.h_q
+    flops = 2 * (cfg.d_qk + cfg.d_v) * pairs
+    return {"bytes": kv + qb + ob, "kv_bytes": kv, "flops": flops, "rows": rows}
+
+
+def stored_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "hbm_traffic_mla_decode_dsv3_b64.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m1 = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    m2 = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    if not (m1 and m2):
+        return None
+    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    return int(m1.group(1)) if m2.group(1) == cur else None
+
+
+def cpu_baseline(d, budget_s=20.0):
+    """The oracle as it stands, on the host cores, over as many whole
+    sequences of the workload as fit in about budget_s seconds."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads = len(os.sched_getaffinity(0))
+    cfg = d["cfg"]
+    done, t0 = 0, time.perf_counter()
+    while done < cfg.batch and time.perf_counter() - t0 < budget_s:
+        idx = [done]
+        q = d["q"][idx]
+        bt = d["block_table"][idx]
+        L = d["cache_seqlens"][idx]
+        if cfg.kind == "mla":
+            oracle.attend_two_pass(q, d["kv"], bt, L, cfg.scale, cfg.causal, d_v=cfg.d_v)
+        else:
+            oracle.attend_two_pass(q, d["k"], bt, L, cfg.scale, cfg.causal, v_cache=d["v"])
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done * cfg.s_q / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {cfg.batch} sequences of the same workload "
+                      f"({done * cfg.s_q} query tokens, {dt:.1f} s, fp64 numpy)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs the decode on one GPU only; "
+              "--gpus above 1 is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_paged_kv_03_amd as lib
+    from mla_paged_kv_03_amd import _lib
+    from workloads import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    L = _lib.lib()
+    sets = []
+    for r in range(args.rotate):
+        # rotated sets share the first set's lengths (same work), not its values
+        d = make_inputs(cfg, seed=cfg.seed + 1000 * r,
+                        seqlens=sets[0][0]["cache_seqlens"] if sets else None)
+        t = {"q": torch.from_numpy(d["q"].view(np.int16)).view(torch.bfloat16).to(dev),
+             "bt": torch.from_numpy(d["block_table"]).to(dev),
+             "sl": torch.from_numpy(d["cache_seqlens"]).to(dev)}
+        for k in ("kv", "k", "v"):
+            if k in d:
+                t[k] = torch.from_numpy(d[k].view(np.int16)).view(torch.bfloat16).to(dev)
+        sets.append((d, t))
+        if r > 0:
+            for k in ("kv", "k", "v"):
+                d.pop(k, None)  # the first set's host copy serves the CPU baseline
+    d0 = sets[0][0]
+    work = algorithmic_work(d0)
+    B, T, H, G = cfg.batch, cfg.s_q, cfg.h_q, cfg.h_kv
+    dv = cfg.d_v
+    plan = lib.mla_decode_plan(sets[0][1]["sl"], T, H, G, dv)
+    info = plan.info
+    out = torch.empty(B, T, H, dv, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=dev)
+    ws, wsb = lib._ws(plan)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda x: ctypes.c_void_p(x.data_ptr())
+    pinfo = ctypes.byref(info)
+
+    def step(i):
+        _, t = sets[i % len(sets)]
+        rc = L.mla_decode_plan(P(t["sl"]), B, T, H, G, dv, P(plan.sched_metadata),
+                               P(plan.num_splits), pinfo, stream)
+        if rc:
+            raise lib.DecodeError("mla_decode_plan", rc)
+        if cfg.kind == "mla":
+            rc = L.mla_decode(P(t["q"]), P(t["kv"]), P(t["bt"]), P(t["sl"]), B, T, H,
+                              t["kv"].shape[0], t["bt"].shape[1], cfg.scale, int(cfg.causal),
+                              P(plan.sched_metadata), P(plan.num_splits), ws, wsb, P(out),
+                              P(lse), stream)
+        else:
+            rc = L.gqa_decode(P(t["q"]), P(t["k"]), P(t["v"]), P(t["bt"]), P(t["sl"]), B, T,
+                              H, G, t["k"].shape[0], t["bt"].shape[1], cfg.scale,
+                              int(cfg.causal), P(plan.sched_metadata), P(plan.num_splits), ws,
+                              wsb, P(out), P(lse), stream)
+        if rc:
+            raise lib.DecodeError("decode", rc)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # timed region: whole steps, and the decode kernel alone via the
+    # library's event hook (events recorded on the kernel's own stream)
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K):
+        lib.profile_events(ev[i][0], ev[i][1])
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    lib.profile_events(None, None)
+    ms_step = t_start.elapsed_time(t_end) / K
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    kern_avg = float(kern_ms.mean())
+
+    # same loop without the event hook: the step rate with nothing extra
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step_plain = t_start.elapsed_time(t_end) / K
+    ms_step = min(ms_step, ms_step_plain)
+    print(f"[bench] {K} steps: {ms_step * 1e3:.1f} us/step, decode kernel "
+          f"{kern_avg * 1e3:.1f} us (median {np.median(kern_ms) * 1e3:.1f})",
+          file=sys.stderr, flush=True)
+
+    s = ms_step * 1e-3
+    tflops = work["flops"] / s / 1e12
+    gbs = work["bytes"] / s / 1e9
+    k_gbs = work["bytes"] / (kern_avg * 1e-3) / 1e9
+    k_tflops = work["flops"] / (kern_avg * 1e-3) / 1e12
+    traffic = stored_traffic()
+    bound = "hbm" if work["flops"] / work["bytes"] < MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 \
+        else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic}
+    roof["kernel"] = f"decode_kernel ({'gqa' if cfg.kind == 'gqa' else 'mla'})"
+    roof["kernel_avg_us"] = round(kern_avg * 1e3, 2)
+    roof["algorithmic_bytes_per_launch"] = work["bytes"]
+    roof["algorithmic_flops_per_launch"] = work["flops"]
+
+    res = {
+        "metric": METRIC,
+        "value": round(B * T / s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "s_q": T, "h_q": H, "h_kv": G,
+                   "d_qk": cfg.d_qk, "d_v": dv, "page": 64, "causal": cfg.causal,
+                   "seqlen_total": int(d0["cache_seqlens"].sum()),
+                   "workers": info.num_workers, "input_sets_rotated": args.rotate},
+        "tflops": round(tflops, 2),
+        "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "hbm_gbs": round(gbs, 1),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(d0)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * Paged attention decode on MI355X (gfx950): C interface.
+ *
+ * What is computed. For every sequence b, query token t and query head h:
+ *     out[b,t,h,:] = sum_j softmax_j(scale * q[b,t,h,:] . K_b[j,g,:]) V_b[j,g,:]
+ *     lse[b,t,h]   = ln sum_j exp(scale * q[b,t,h,:] . K_b[j,g,:])
+ * the attention of FlashAttention (KO), section "표준 Attention의 문제점",
+ * computed exactly (section "온라인 Softmax 계산": running max and running
+ * exp-sum) in one fused pass per 64-token page, so the score matrix never
+ * reaches HBM (sections "타일링 및 블록 처리" and "단일 CUDA 커널로의 연산 융합").
+ * j runs over the keys query token t may see: 0 <= j < L_b, and with
+ * causal != 0, j <= L_b - s_q + t (the s_q new tokens are the last s_q of
+ * the L_b cached ones). A row that sees no key gets out = 0, lse = -inf.
+ *
+ * The cache is paged: token j of sequence b lives in physical page
+ * block_table[b, j / 64], slot j % 64 (PagedAttention, cited in the same
+ * article's "참고 문헌"; 64-token pages per the FlashMLA blog, "기술 기반").
+ * Two shapes (GQLA review, "1. Key Terms & Definitions"):
+ *   - mla_decode: MQA-absorb path. One latent KV head; every query head
+ *     attends the same 576-wide row (512 latent + 64 rope) and V is its
+ *     first 512 columns.
+ *   - gqa_decode: GQA path. h_kv KV heads with separate 128-wide K and V;
+ *     query head h uses KV head h / (h_q / h_kv).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless marked (host). The caller owns
+ *     every buffer; the library keeps only a per-device cache of the
+ *     compute-unit count.
+ *   - bf16 tensors are contiguous, row-major in the shapes given, 16-byte
+ *     aligned. int32 tensors are contiguous.
+ *   - Work is enqueued on `stream` (0 = the null stream). No call blocks,
+ *     allocates device memory or copies device data to the host.
+ *   - Return value: MLA_OK (0) or a negative MLA_ERR_* code. Every argument
+ *     check happens before anything is enqueued; on error nothing is.
+ *   - Device-resident data cannot be checked from the host; these are
+ *     preconditions: 0 <= cache_seqlens[b] <= 64 * max_pages_per_seq, and
+ *     0 <= block_table[b, j] < num_pages for j < ceil(cache_seqlens[b] / 64).
+ *     Block-table entries past that (pads, e.g. -1) are never read, and
+ *     neither are page slots at or past cache_seqlens[b].
+ *   - Split-KV: one launch spreads the pages of all sequences evenly over a
+ *     fixed number of workgroups (mla_decode_plan). A sequence whose pages
+ *     land on several workgroups is finished by an internal log-sum-exp
+ *     merge (attn_combine's kernel) inside the same call.
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL_ARG = -1,            /* a required pointer is NULL */
+  MLA_ERR_BAD_SHAPE = -2,           /* negative size, h_q % h_kv != 0, ... */
+  MLA_ERR_UNSUPPORTED = -3,         /* head dims or row counts not built */
+  MLA_ERR_WORKSPACE_TOO_SMALL = -4, /* workspace_bytes below the plan's */
+  MLA_ERR_HIP = -5                  /* a HIP runtime call or launch failed */
+};
+
+/* Host-side description of a decode plan, filled by mla_decode_plan. */
+typedef struct {
+  int32_t num_workers;      /* workgroups that share the pages of the batch */
+  int32_t row_blocks;       /* workgroups per worker (query-row blocks x KV heads) */
+  int32_t max_split_slots;  /* upper bound of partial results (2 * (workers - 1)) */
+  int32_t reserved;
+  size_t metadata_bytes;    /* size of sched_metadata (int32) */
+  size_t num_splits_bytes;  /* size of num_splits: (batch + 1) int32 */
+  size_t workspace_bytes;   /* fp32 partials for split sequences */
+} mla_plan_info;
+
+/* Plan the split-KV schedule of one decode step (FlashAttention (KO),
+ * section "FlashAttention-2 (2023)": better work partitioning across the
+ * GPU; variable lengths per the FlashMLA blog, "기술 기반").
+ *
+ * The concatenated work of the batch, sum_b (ceil(L_b / 64) + 2) units,
+ * is cut into num_workers nearly equal contiguous ranges; a sequence that
+ * straddles a cut is split, and its partial results are merged later.
+ *
+ *   cache_seqlens  int32 [batch], device.
+ *   batch, s_q, h_q, h_kv, head_dim_v: shape of the step (h_kv = 1 and
+ *                  head_dim_v = 512 for mla_decode; h_kv > 1 and
+ *                  head_dim_v = 128 for gqa_decode).
+ *   sched_metadata int32 buffer of info->metadata_bytes (out).
+ *   num_splits     int32 [batch + 1] (out): num_splits[b + 1] - num_splits[b]
+ *                  is the number of partial results of sequence b (0 when
+ *                  it is not split); num_splits[b] is its first slot.
+ *   info           (host, out) sizes; required.
+ *
+ * With sched_metadata and num_splits both NULL only *info is filled and
+ * nothing is enqueued, so callers can size buffers first. The sizes depend
+ * only on the shape arguments and the current device. The plan may be
+ * reused by every layer of the step (same cache_seqlens and shape).
+ */
+int mla_decode_plan(const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
+                    int32_t h_q, int32_t h_kv, int32_t head_dim_v,
+                    int32_t* sched_metadata, int32_t* num_splits,
+                    mla_plan_info* info, hipStream_t stream);
+
+/* MLA decode, MQA-absorb path (GQLA review, "1. Key Terms & Definitions").
+ *
+ *   q              bf16 [batch, s_q, h_q, 576]
+ *   kv_cache       bf16 [num_pages, 64, 1, 576]; V = columns 0..511
+ *   block_table    int32 [batch, max_pages_per_seq]
+ *   cache_seqlens  int32 [batch]
+ *   softmax_scale  multiplies q.k before the softmax (1/sqrt(192) for
+ *                  DeepSeek-V3 shapes)
+ *   causal         0 or 1, see the top of this file
+ *   sched_metadata, num_splits: from mla_decode_plan with the same
+ *                  cache_seqlens, batch, s_q, h_q, h_kv = 1, head_dim_v = 512
+ *   workspace      device scratch of at least info.workspace_bytes (may be
+ *                  NULL when that is 0); contents on entry do not matter
+ *   out            bf16 [batch, s_q, h_q, 512] (out)
+ *   lse            fp32 [batch, s_q, h_q] (out), natural log
+ * Supported: 1 <= s_q * h_q <= 2^20; rows are cut into blocks of 64.
+ */
+int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+               const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+               int32_t num_pages, int32_t max_pages_per_seq, float softmax_scale,
+               int32_t causal, const int32_t* sched_metadata, const int32_t* num_splits,
+               void* workspace, size_t workspace_bytes, void* out, float* lse,
+               hipStream_t stream);
+
+/* GQA decode with a per-group expanded cache (GQLA review, "1. Key Terms &
+ * Definitions", GQA path).
+ *
+ *   q              bf16 [batch, s_q, h_q, 128]
+ *   k_cache        bf16 [num_pages, 64, h_kv, 128]
+ *   v_cache        bf16 [num_pages, 64, h_kv, 128]
+ *   out            bf16 [batch, s_q, h_q, 128] (out); lse fp32 [batch, s_q, h_q]
+ *   The plan must come from mla_decode_plan with the same h_kv and
+ *   head_dim_v = 128. Other arguments as for mla_decode.
+ * Supported: h_q % h_kv == 0, any s_q * h_q / h_kv >= 1.
+ */
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+               int32_t s_q, int32_t h_q, int32_t h_kv, int32_t num_pages,
+               int32_t max_pages_per_seq, float softmax_scale, int32_t causal,
+               const int32_t* sched_metadata, const int32_t* num_splits, void* workspace,
+               size_t workspace_bytes, void* out, float* lse, hipStream_t stream);
+
+/* Merge partial attention results computed over disjoint key subsets of
+ * the same rows (follows from the online-softmax statistics of
+ * FlashAttention (KO), "온라인 Softmax 계산"): for every row with n >= 1
+ * partials, lse = m + ln sum_i exp(lse_i - m) with m = max_i lse_i, and
+ * out = sum_i exp(lse_i - lse) o_i; partials with lse_i = -inf add nothing,
+ * and a row whose partials are all -inf gets out = 0, lse = -inf.
+ *
+ *   o_partial    fp32 [num_slots, rows_per_batch, dv], each partial already
+ *                normalised over its own keys
+ *   lse_partial  fp32 [num_slots, rows_per_batch], natural log
+ *   num_splits   int32 [batch + 1], device: sequence b owns slots
+ *                num_splits[b] .. num_splits[b + 1] - 1; a sequence with no
+ *                slot is left untouched in out and lse
+ *   out          bf16 [batch, rows_per_batch, dv] (out)
+ *   lse          fp32 [batch, rows_per_batch] (out)
+ * dv must be a multiple of 8, at most 1024.
+ */
+int attn_combine(const float* o_partial, const float* lse_partial, const int32_t* num_splits,
+                 int32_t batch, int32_t rows_per_batch, int32_t dv, void* out, float* lse,
+                 hipStream_t stream);
+
+/* The plan's schedule computed on the host from host-resident lengths, for
+ * checking the schedule on a machine without a GPU. num_workers, the
+ * metadata layout and num_splits are exactly those mla_decode_plan would
+ * write for the same arguments on a device with `num_cus` compute units.
+ * seqlens_host, sched_metadata_host, num_splits_host and info are host
+ * pointers. */
+int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q, int32_t h_q,
+                         int32_t h_kv, int32_t head_dim_v, int32_t num_cus,
+                         int32_t* sched_metadata_host, int32_t* num_splits_host,
+                         mla_plan_info* info);
+
+/* Profiling hook: while set, every mla_decode / gqa_decode call records the
+ * HIP event `start` on its stream right before its main decode kernel and
+ * `stop` right after it (before any merge kernel), so a caller can time that
+ * kernel alone. Both are hipEvent_t handles; NULL clears the hook. Process-
+ * wide and not thread-safe: meant for benchmarks, not for serving. */
+void mla_profile_events(void* start, void* stop);
+
+/* A short English text for a return code (static storage). */
+const char* mla_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */

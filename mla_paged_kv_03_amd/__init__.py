@@ -1,0 +1,202 @@
+"""Paged MLA / GQA attention decode on MI355X (gfx950).
+
+Thin Python binding over the C interface in include/mla_decode.h: the
+functions below only check and marshal torch tensors (device pointers and
+the current HIP stream); every step of the decode runs in the library's HIP
+kernels. There is no CPU fallback: without the built library the import of
+the native code fails loudly.
+
+    plan = mla_decode_plan(cache_seqlens, s_q, h_q, h_kv=1, head_dim_v=512)
+    out, lse = mla_decode(q, kv_cache, block_table, cache_seqlens, scale, causal, plan)
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import DecodeError, PlanInfo
+
+__all__ = ["Plan", "PlanInfo", "DecodeError", "plan_info", "mla_decode_plan", "mla_decode",
+           "gqa_decode", "attn_combine", "mla_decode_plan_host", "profile_events"]
+
+MLA_D, MLA_DV = 576, 512
+GQA_D = 128
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+@dataclass
+class Plan:
+    """A split-KV schedule for one decode step (reusable across layers)."""
+    sched_metadata: torch.Tensor
+    num_splits: torch.Tensor
+    info: PlanInfo
+    workspace: torch.Tensor | None
+    shape: tuple  # (batch, s_q, h_q, h_kv, head_dim_v)
+
+
+def plan_info(batch, s_q, h_q, h_kv=1, head_dim_v=MLA_DV) -> PlanInfo:
+    """Buffer sizes of a plan on the current device (no device work)."""
+    info = PlanInfo()
+    _lib.check("mla_decode_plan", _lib.lib().mla_decode_plan(
+        None, batch, s_q, h_q, h_kv, head_dim_v, None, None, ctypes.byref(info), None))
+    return info
+
+
+def mla_decode_plan(cache_seqlens, s_q, h_q, h_kv=1, head_dim_v=MLA_DV) -> Plan:
+    """Allocate the plan's buffers (metadata, num_splits, workspace) and
+    enqueue the plan kernel on the current stream."""
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    batch = cache_seqlens.shape[0]
+    info = plan_info(batch, s_q, h_q, h_kv, head_dim_v)
+    dev = cache_seqlens.device
+    meta = torch.empty(info.metadata_bytes // 4, dtype=torch.int32, device=dev)
+    splits = torch.empty(batch + 1, dtype=torch.int32, device=dev)
+    ws = (torch.empty(info.workspace_bytes // 4 + 64, dtype=torch.float32, device=dev)
+          if info.workspace_bytes else None)
+    _lib.check("mla_decode_plan", _lib.lib().mla_decode_plan(
+        _ptr(cache_seqlens), batch, s_q, h_q, h_kv, head_dim_v, _ptr(meta), _ptr(splits),
+        ctypes.byref(info), _stream()))
+    return Plan(meta, splits, info, ws, (batch, s_q, h_q, h_kv, head_dim_v))
+
+
+def _ws(plan):
+    if plan.workspace is None:
+        return None, 0
+    # 256-byte aligned start inside the allocation
+    p = plan.workspace.data_ptr()
+    off = (-p) % 256
+    return ctypes.c_void_p(p + off), plan.workspace.numel() * 4 - off
+
+
+def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal=False,
+               plan: Plan | None = None, out=None, lse=None):
+    """MQA-absorb MLA decode. q bf16 [B, s_q, h_q, 576]; kv_cache bf16
+    [num_pages, 64, 1, 576]; block_table int32 [B, max_pages]; cache_seqlens
+    int32 [B]. Returns (out bf16 [B, s_q, h_q, 512], lse fp32 [B, s_q, h_q])."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv_cache, "kv_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, T, H, D = q.shape
+    if D != MLA_D or tuple(kv_cache.shape[1:]) != (64, 1, MLA_D):
+        raise ValueError("mla_decode expects q [..., 576] and kv_cache [P, 64, 1, 576]")
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("batch mismatch")
+    if plan is None:
+        plan = mla_decode_plan(cache_seqlens, T, H, 1, MLA_DV)
+    if plan.shape != (B, T, H, 1, MLA_DV):
+        raise ValueError(f"plan was made for {plan.shape}")
+    if out is None:
+        out = torch.empty(B, T, H, MLA_DV, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    ws, wsb = _ws(plan)
+    _lib.check("mla_decode", _lib.lib().mla_decode(
+        _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens), B, T, H,
+        kv_cache.shape[0], block_table.shape[1], float(softmax_scale), int(bool(causal)),
+        _ptr(plan.sched_metadata), _ptr(plan.num_splits), ws, wsb, _ptr(out), _ptr(lse),
+        _stream()))
+    return out, lse
+
+
+def gqa_decode(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal=False,
+               plan: Plan | None = None, out=None, lse=None):
+    """GQA decode with a per-group expanded cache. q bf16 [B, s_q, h_q, 128];
+    k_cache, v_cache bf16 [num_pages, 64, h_kv, 128]."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, T, H, D = q.shape
+    P, page, G, Dk = k_cache.shape
+    if D != GQA_D or Dk != GQA_D or page != 64 or tuple(v_cache.shape) != (P, 64, G, GQA_D):
+        raise ValueError("gqa_decode expects q [..., 128] and k/v caches [P, 64, h_kv, 128]")
+    if plan is None:
+        plan = mla_decode_plan(cache_seqlens, T, H, G, GQA_D)
+    if plan.shape != (B, T, H, G, GQA_D):
+        raise ValueError(f"plan was made for {plan.shape}")
+    if out is None:
+        out = torch.empty(B, T, H, GQA_D, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    ws, wsb = _ws(plan)
+    _lib.check("gqa_decode", _lib.lib().gqa_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens), B, T, H,
+        G, P, block_table.shape[1], float(softmax_scale), int(bool(causal)),
+        _ptr(plan.sched_metadata), _ptr(plan.num_splits), ws, wsb, _ptr(out), _ptr(lse),
+        _stream()))
+    return out, lse
+
+
+def attn_combine(o_partial, lse_partial, num_splits, out=None, lse=None):
+    """Log-sum-exp merge of partials. o_partial fp32 [slots, R, dv],
+    lse_partial fp32 [slots, R], num_splits int32 [B + 1] (slot prefix).
+    Returns out bf16 [B, R, dv], lse fp32 [B, R] (rows of sequences without
+    slots are left as given)."""
+    _need(o_partial, "o_partial", torch.float32, 3)
+    _need(lse_partial, "lse_partial", torch.float32, 2)
+    _need(num_splits, "num_splits", torch.int32, 1)
+    _, R, dv = o_partial.shape
+    B = num_splits.shape[0] - 1
+    if out is None:
+        out = torch.zeros(B, R, dv, dtype=torch.bfloat16, device=o_partial.device)
+    if lse is None:
+        lse = torch.full((B, R), float("-inf"), dtype=torch.float32, device=o_partial.device)
+    _lib.check("attn_combine", _lib.lib().attn_combine(
+        _ptr(o_partial), _ptr(lse_partial), _ptr(num_splits), B, R, dv, _ptr(out), _ptr(lse),
+        _stream()))
+    return out, lse
+
+
+def mla_decode_plan_host(seqlens, s_q, h_q, h_kv=1, head_dim_v=MLA_DV, num_cus=256):
+    """The plan computed on the host (for checking the schedule without a
+    GPU). seqlens: sequence of ints. Returns (metadata, num_splits, info) as
+    Python lists and a PlanInfo."""
+    import numpy as np
+    L = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    info = PlanInfo()
+    lib = _lib.lib()
+    _lib.check("mla_decode_plan_host", lib.mla_decode_plan_host(
+        L.ctypes.data_as(ctypes.c_void_p), len(L), s_q, h_q, h_kv, head_dim_v, num_cus, None,
+        None, ctypes.byref(info)))
+    meta = np.zeros(info.metadata_bytes // 4, dtype=np.int32)
+    splits = np.zeros(len(L) + 1, dtype=np.int32)
+    _lib.check("mla_decode_plan_host", lib.mla_decode_plan_host(
+        L.ctypes.data_as(ctypes.c_void_p), len(L), s_q, h_q, h_kv, head_dim_v, num_cus,
+        meta.ctypes.data_as(ctypes.c_void_p), splits.ctypes.data_as(ctypes.c_void_p),
+        ctypes.byref(info)))
+    return meta, splits, info
+
+
+def profile_events(start=None, stop=None):
+    """Record `start` / `stop` (torch.cuda.Event) around the main decode
+    kernel of every following decode call on its stream; None clears."""
+    _lib.lib().mla_profile_events(
+        ctypes.c_void_p(start.cuda_event) if start is not None else None,
+        ctypes.c_void_p(stop.cuda_event) if stop is not None else None)

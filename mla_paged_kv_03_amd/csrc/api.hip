@@ -1,0 +1,275 @@
+// C interface: argument checks, launch geometry and kernel launches.
+// Every check runs before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/mla_decode.h"
+#include "kernels.h"
+#include "schedule.h"
+
+namespace {
+
+constexpr int MLA_D = 576, MLA_DV = 512;  // latent row: 512 latent + 64 rope
+constexpr int GQA_D = 128, GQA_DV = 128;
+constexpr int MAX_DEVICES = 64;
+int g_cu_count[MAX_DEVICES];  // 0 = not queried yet
+hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;  // mla_profile_events
+
+int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev >= 0 && dev < MAX_DEVICES && g_cu_count[dev] > 0) {
+    *cus = g_cu_count[dev];
+    return MLA_OK;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return MLA_ERR_HIP;
+  if (dev >= 0 && dev < MAX_DEVICES) g_cu_count[dev] = n;
+  *cus = n;
+  return MLA_OK;
+}
+
+struct Geom {
+  bool gqa;
+  int B, T, H, G, D, DV;
+  int M;      // query rows per KV head
+  int nw;     // row groups of 16 rows per workgroup (1, 2 or 4)
+  int nrb;    // row blocks per KV head
+  int RB;     // row blocks per worker (all KV heads)
+  int W;      // workers
+  int TH;
+  int max_slots;
+  size_t meta_bytes, split_bytes, ws_bytes, lse_offset;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int make_geom(int B, int T, int H, int G, int DV, int cus, Geom* g) {
+  if (B < 0 || T < 1 || H < 1 || G < 1 || H % G != 0) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)T * H > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+  memset(g, 0, sizeof(*g));
+  if (DV == MLA_DV) {
+    if (G != 1) return MLA_ERR_UNSUPPORTED;
+    g->gqa = false;
+    g->D = MLA_D;
+  } else if (DV == GQA_DV) {
+    g->gqa = true;
+    g->D = GQA_D;
+  } else {
+    return MLA_ERR_UNSUPPORTED;
+  }
+  g->B = B; g->T = T; g->H = H; g->G = G; g->DV = DV;
+  g->M = T * H / G;
+  g->nw = g->M <= 16 ? 1 : g->M <= 32 ? 2 : 4;
+  const int rows = 16 * g->nw;
+  g->nrb = (g->M + rows - 1) / rows;
+  g->RB = G * g->nrb;
+  // one workgroup per CU for the latent cache (two 72 KiB page buffers);
+  // the GQA pages are 32 KiB, so two workgroups share a CU
+  const int per_cu = g->gqa ? 2 : 1;
+  int W = cus * per_cu / g->RB;
+  if (W >= 8) W -= W % 8;
+  if (W < 1) W = 1;
+  g->W = W;
+  g->TH = T * H;
+  g->max_slots = 2 * (W - 1);
+  g->meta_bytes = ((size_t)W * sched::REC + (size_t)B + 1) * sizeof(int32_t);
+  g->split_bytes = ((size_t)B + 1) * sizeof(int32_t);
+  const size_t o_bytes = (size_t)g->max_slots * g->TH * DV * sizeof(float);
+  const size_t l_bytes = (size_t)g->max_slots * g->TH * sizeof(float);
+  g->lse_offset = align256(o_bytes);
+  g->ws_bytes = g->max_slots ? g->lse_offset + l_bytes : 0;
+  return MLA_OK;
+}
+
+void fill_info(const Geom& g, mla_plan_info* info) {
+  info->num_workers = g.W;
+  info->row_blocks = g.RB;
+  info->max_split_slots = g.max_slots;
+  info->reserved = 0;
+  info->metadata_bytes = g.meta_bytes;
+  info->num_splits_bytes = g.split_bytes;
+  info->workspace_bytes = g.ws_bytes;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Pointer and value checks that need no device query.
+int check_decode_args(bool gqa, const void* q, const void* k, const void* v,
+                      const int32_t* block_table, const int32_t* seqlens, int num_pages,
+                      int max_pages, float scale, int causal, const int32_t* meta,
+                      const int32_t* splits, const void* out, const float* lse) {
+  if (!q || !k || (gqa && !v) || !block_table || !seqlens || !meta || !splits || !out || !lse)
+    return MLA_ERR_NULL_ARG;
+  if (num_pages < 1 || max_pages < 1) return MLA_ERR_BAD_SHAPE;
+  if (!(scale == scale) || isinf(scale)) return MLA_ERR_BAD_SHAPE;
+  if (causal != 0 && causal != 1) return MLA_ERR_BAD_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || (v && !aligned16(v)) || !aligned16(out))
+    return MLA_ERR_BAD_SHAPE;
+  return MLA_OK;
+}
+
+int run_decode(int B, int T, int H, int G, int DV, const void* q, const void* k, const void* v,
+               const int32_t* block_table, const int32_t* seqlens, int num_pages,
+               int max_pages, float scale, int causal, const int32_t* meta,
+               const int32_t* splits, void* ws, size_t ws_bytes, void* out, float* lse,
+               hipStream_t st) {
+  Geom g;
+  int rc, cus = 0;
+  if ((rc = make_geom(B, T, H, G, DV, 1, &g)) != MLA_OK) return rc;
+  if (B == 0) return MLA_OK;  // nothing to read or write (buffers may be empty)
+  if ((rc = check_decode_args(g.gqa, q, k, v, block_table, seqlens, num_pages, max_pages, scale,
+                              causal, meta, splits, out, lse)) != MLA_OK)
+    return rc;
+  if ((rc = device_cus(&cus)) != MLA_OK) return rc;
+  make_geom(B, T, H, G, DV, cus, &g);
+  if (g.ws_bytes) {
+    if (!ws) return MLA_ERR_NULL_ARG;
+    if (ws_bytes < g.ws_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (((uintptr_t)ws & 255) != 0) return MLA_ERR_BAD_SHAPE;
+  }
+
+  mla::DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.block_table = block_table;
+  a.seqlens = seqlens;
+  a.meta = meta;
+  a.slots = splits;
+  a.part_o = (float*)ws;
+  a.part_lse = ws ? (float*)((char*)ws + g.lse_offset) : nullptr;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.B = g.B; a.T = g.T; a.H = g.H; a.G = g.G; a.bt_stride = max_pages;
+  a.M = g.M; a.nrb = g.nrb; a.W = g.W;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.causal = causal;
+  if (g_prof_start && hipEventRecord(g_prof_start, st) != hipSuccess) return MLA_ERR_HIP;
+  if (mla::launch_decode_kernel(a, g.nw, g.gqa, g.W * g.RB, st) != hipSuccess) return MLA_ERR_HIP;
+  if (g_prof_stop && hipEventRecord(g_prof_stop, st) != hipSuccess) return MLA_ERR_HIP;
+  if (g.max_slots > 0) {
+    mla::CombineArgs c;
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.slots = splits;
+    c.out = a.out;
+    c.lse = lse;
+    c.B = g.B; c.R = g.TH; c.DV = g.DV;
+    if (mla::launch_combine_kernel(c, st) != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_plan(const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                    int32_t h_kv, int32_t head_dim_v, int32_t* sched_metadata,
+                    int32_t* num_splits, mla_plan_info* info, hipStream_t stream) {
+  if (!info) return MLA_ERR_NULL_ARG;
+  int cus = 0, rc;
+  Geom g;
+  if ((rc = make_geom(batch, s_q, h_q, h_kv, head_dim_v, 1, &g)) != MLA_OK) return rc;
+  if ((sched_metadata || num_splits) &&
+      (!sched_metadata || !num_splits || (batch > 0 && !cache_seqlens)))
+    return MLA_ERR_NULL_ARG;
+  if ((rc = device_cus(&cus)) != MLA_OK) return rc;
+  make_geom(batch, s_q, h_q, h_kv, head_dim_v, cus, &g);
+  fill_info(g, info);
+  if (!sched_metadata && !num_splits) return MLA_OK;
+  if (mla::launch_plan_kernel(cache_seqlens, batch, g.W, sched_metadata, num_splits, stream) !=
+      hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+               const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+               int32_t num_pages, int32_t max_pages_per_seq, float softmax_scale,
+               int32_t causal, const int32_t* sched_metadata, const int32_t* num_splits,
+               void* workspace, size_t workspace_bytes, void* out, float* lse,
+               hipStream_t stream) {
+  return run_decode(batch, s_q, h_q, 1, MLA_DV, q, kv_cache, nullptr, block_table, cache_seqlens, num_pages,
+                    max_pages_per_seq, softmax_scale, causal, sched_metadata, num_splits,
+                    workspace, workspace_bytes, out, lse, stream);
+}
+
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+               int32_t s_q, int32_t h_q, int32_t h_kv, int32_t num_pages,
+               int32_t max_pages_per_seq, float softmax_scale, int32_t causal,
+               const int32_t* sched_metadata, const int32_t* num_splits, void* workspace,
+               size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
+  return run_decode(batch, s_q, h_q, h_kv, GQA_DV, q, k_cache, v_cache, block_table, cache_seqlens, num_pages,
+                    max_pages_per_seq, softmax_scale, causal, sched_metadata, num_splits,
+                    workspace, workspace_bytes, out, lse, stream);
+}
+
+int attn_combine(const float* o_partial, const float* lse_partial, const int32_t* num_splits,
+                 int32_t batch, int32_t rows_per_batch, int32_t dv, void* out, float* lse,
+                 hipStream_t stream) {
+  if (batch < 0 || rows_per_batch < 0 || dv < 8 || dv > 1024 || dv % 8) return MLA_ERR_BAD_SHAPE;
+  if (batch == 0 || rows_per_batch == 0) return MLA_OK;
+  if (!o_partial || !lse_partial || !num_splits || !out || !lse) return MLA_ERR_NULL_ARG;
+  if (!aligned16(o_partial) || !aligned16(out)) return MLA_ERR_BAD_SHAPE;
+  mla::CombineArgs c;
+  c.part_o = o_partial;
+  c.part_lse = lse_partial;
+  c.slots = num_splits;
+  c.out = (uint16_t*)out;
+  c.lse = lse;
+  c.B = batch; c.R = rows_per_batch; c.DV = dv;
+  return mla::launch_combine_kernel(c, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q, int32_t h_q,
+                         int32_t h_kv, int32_t head_dim_v, int32_t num_cus,
+                         int32_t* sched_metadata_host, int32_t* num_splits_host,
+                         mla_plan_info* info) {
+  if (!info) return MLA_ERR_NULL_ARG;
+  if (num_cus < 1) return MLA_ERR_BAD_SHAPE;
+  Geom g;
+  int rc;
+  if ((rc = make_geom(batch, s_q, h_q, h_kv, head_dim_v, num_cus, &g)) != MLA_OK) return rc;
+  fill_info(g, info);
+  if (!sched_metadata_host && !num_splits_host) return MLA_OK;
+  if (!sched_metadata_host || !num_splits_host || (batch > 0 && !seqlens_host))
+    return MLA_ERR_NULL_ARG;
+  int32_t* prefix = sched_metadata_host + (size_t)g.W * sched::REC;
+  prefix[0] = 0;
+  for (int b = 0; b < batch; ++b) prefix[b + 1] = prefix[b] + sched::seq_units(seqlens_host[b]);
+  for (int w = 0; w < g.W; ++w)
+    sched::worker_record(w, g.W, prefix, seqlens_host, batch,
+                         sched_metadata_host + (size_t)w * sched::REC);
+  int32_t acc = 0;
+  for (int b = 0; b < batch; ++b) {
+    num_splits_host[b] = acc;
+    acc += sched::seq_slots(b, g.W, prefix, seqlens_host, batch);
+  }
+  num_splits_host[batch] = acc;
+  return MLA_OK;
+}
+
+void mla_profile_events(void* start, void* stop) {
+  g_prof_start = (hipEvent_t)start;
+  g_prof_stop = (hipEvent_t)stop;
+}
+
+const char* mla_status_string(int code) {
+  switch (code) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case MLA_ERR_BAD_SHAPE: return "invalid shape, alignment or argument value";
+    case MLA_ERR_UNSUPPORTED: return "head dimensions or sizes not supported by this build";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the plan requires";
+    case MLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

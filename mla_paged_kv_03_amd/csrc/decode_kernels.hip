@@ -1,0 +1,506 @@
+// Fused paged attention decode for gfx950: one kernel walks a worker's
+// pages, and per 64-token page computes scores on MFMA, masks them, updates
+// the online softmax and accumulates P V on MFMA, writing only the final
+// (or split-partial) result.
+//
+// Method: FlashAttention (KO) — tiling ("타일링 및 블록 처리"), the online
+// softmax with a running max and running exp-sum ("온라인 Softmax 계산"), and
+// one fused kernel for QK^T, masking, softmax and the product with V
+// ("단일 CUDA 커널로의 연산 융합"). Paging: PagedAttention's block table
+// (cited in "참고 문헌") with 64-token pages (FlashMLA blog, "기술 기반").
+// Shapes: the MQA-absorb and GQA decode paths of the GQLA review ("1. Key
+// Terms & Definitions").
+//
+// Work layout (gfx950, wave64, 4 waves per workgroup):
+//   * A workgroup owns one worker's range of pages (schedule.h) for one KV
+//     head g and a block of 16*R query rows that share that head. Wave w
+//     owns 16 rows (row group w % R); the KS = 4 / R waves of a row group
+//     split every page's 64 keys into KS parts and keep separate softmax
+//     states, merged through LDS when the worker's range of a sequence ends.
+//   * Pages stream HBM -> LDS with global_load_lds_dwordx4 (no staging
+//     registers), double-buffered: the next page is in flight while the
+//     current one is computed.
+//   * Scores are computed transposed, S^T[key][row] = K . Q^T, on 16x16x32
+//     bf16 MFMA: lane l holds query row l % 16 and four keys per 16-key
+//     block, so the row max and sum are in-lane reductions plus two
+//     exchanges across the four 16-lane groups.
+//   * Those registers, rounded to bf16, are directly the B operand of
+//     O^T[dv][row] += V^T . P^T: an MFMA sums over its K slots in any order
+//     as long as both operands agree, so the key in slot i of lane l is the
+//     key that lane's score register already holds. The V^T operand is read
+//     from the same LDS page with ds_read_b64_tr_b16 (4 consecutive keys of
+//     one column per lane); for the latent cache V is columns 0..511 of the
+//     K rows already in LDS, so every cache byte crosses HBM once.
+//   * Q (72 registers) stays in registers for the whole sequence; O^T (128
+//     fp32 registers for 512 columns) accumulates in registers.
+#include "device_common.h"
+#include "kernels.h"
+#include "schedule.h"
+
+namespace mla {
+
+// Map a workgroup id to (worker, row block). Workgroups are dispatched to
+// the 8 XCDs round-robin, so the row blocks of one worker (which read the
+// same pages) get ids congruent mod 8 and share an XCD's L2.
+__device__ __forceinline__ void decode_block_id(int bid, int W, int RB, int& w, int& rb) {
+  if ((W & 7) == 0) {
+    const int group = bid / (8 * RB);
+    const int rem = bid - group * 8 * RB;
+    rb = rem >> 3;
+    w = group * 8 + (rem & 7);
+  } else {
+    w = bid / RB;
+    rb = bid - w * RB;
+  }
+}
+
+// LDS page layouts (bytes). Row k of a region with P bytes per row keeps its
+// 16-byte chunk c at k * P + 16 * (c ^ swz(k)).
+template <bool GQA>
+struct Layout;
+
+// Latent cache: 576-wide rows split as columns 0..511 (latent, which is also
+// V) and 512..575 (rope).
+template <>
+struct Layout<false> {
+  static constexpr int D = 576, DV = 512;
+  static constexpr int TILE = 64 * 1152;  // one page
+  static constexpr int K_PITCH = 1024;    // latent region: 64 chunks per row
+  static constexpr int ROPE = 65536;      // rope region: 8 chunks per row
+  static constexpr int ROPE_PITCH = 128;
+  static constexpr int V_BASE = 0, V_PITCH = 1024;
+  static constexpr int DMA_PER_TILE = 72;  // 1 KiB per instruction
+};
+
+// GQA: separate 128-wide K and V rows of one KV head.
+template <>
+struct Layout<true> {
+  static constexpr int D = 128, DV = 128;
+  static constexpr int TILE = 2 * 64 * 256;
+  static constexpr int K_PITCH = 256;
+  static constexpr int ROPE = 0, ROPE_PITCH = 0;
+  static constexpr int V_BASE = 64 * 256, V_PITCH = 256;
+  static constexpr int DMA_PER_TILE = 32;
+};
+
+// Issue one 1 KiB HBM -> LDS copy: lane l's 16 bytes at sbase + voff land at
+// LDS byte lds + 16 * l. Issued from inline asm so that the compiler does not
+// add its own conservative wait on the asynchronous LDS write; the kernel
+// waits with explicit vmcnt counts.
+__device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// Softmax weights may exceed 1 by up to 2^RESCALE_SLACK before O is rescaled.
+constexpr float RESCALE_SLACK = 8.f;
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Keeps the compiler from moving memory operations across this point (it
+// bounds how far LDS reads are hoisted ahead of the MFMAs that use them).
+__device__ __forceinline__ void mem_fence_compiler() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uintptr_t u = (uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const T*)(((uintptr_t)hi << 32) | lo);
+}
+
+// Scalar load of one int32 from a wave-uniform address. The wait sits in the
+// same asm statement, so the result is ready when the statement ends; it is
+// a scalar-cache load and does not touch vmcnt, which counts page copies.
+__device__ __forceinline__ int sload(const int32_t* p) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float max4groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum4groups(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
+}
+
+template <int R, bool GQA>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  using LY = Layout<GQA>;
+  constexpr int NW = 4;
+  constexpr int KS = NW / R;      // waves sharing a row group (key split)
+  constexpr int KW = 64 / KS;     // keys per wave per page
+  constexpr int KB = KW / 16;     // 16-key score blocks per wave per page
+  constexpr int D = LY::D, DV = LY::DV;
+  constexpr int KC = D / 32;      // MFMA K steps of the score product
+  constexpr int NCB = DV / 16;    // 16-wide column blocks of the output
+  constexpr int ROWS = 16 * R;
+  constexpr int NDMA = LY::DMA_PER_TILE / NW;  // per wave per page
+  static_assert(LY::DMA_PER_TILE % NW == 0 && NDMA < 64, "page copies split evenly");
+
+  __shared__ __attribute__((aligned(1024))) char lds[2 * LY::TILE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, lds);
+
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 15;     // query row within the wave's 16
+  const int g4 = lane >> 4;    // 16-lane group
+  const int rg = wave % R;     // row group
+  const int ks = wave / R;     // key part
+
+  int w, rb;
+  decode_block_id(blockIdx.x, a.W, a.G * a.nrb, w, rb);
+  const int g = rb / a.nrb;
+  const int rblk = rb - g * a.nrb;
+
+  const int32_t* rec = a.meta + w * sched::REC;
+  const int bs = uniform(rec[sched::R_B_START]);
+  const int be = uniform(rec[sched::R_B_END]);
+  if (be < bs) return;
+
+  const int hpg = a.H / a.G;
+  const int r = rblk * ROWS + rg * 16 + n;  // row within this KV head
+  const bool row_ok = r < a.M;
+  const int t = row_ok ? r / hpg : 0;
+  const int h = g * hpg + (row_ok ? r - t * hpg : 0);
+  const int rho = t * a.H + h;               // output row within a sequence
+  const int TH = a.T * a.H;
+
+  // ---- per-lane LDS offsets (bytes, relative to a page buffer) ----
+  // score operand: key ks*KW + 16kb + n, 16-byte chunk 4c + g4 of the K row
+  const int fn = swz(n & 7);
+  uint32_t qk_off[2], rope_off[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    qk_off[p] = (ks * KW + n) * LY::K_PITCH + 16 * ((4 * p + g4) ^ fn);
+    rope_off[p] = LY::ROPE + (ks * KW + n) * LY::ROPE_PITCH + 16 * ((4 * p + g4) ^ fn);
+  }
+  // V^T operand by transposed reads: 16-lane group g4 reads keys
+  // 4*g4 + (j>>2) (+ a multiple of 16) at columns 16cb + 4(j&3) .. +3
+  const int j16 = lane & 15;
+  const int vkey = 4 * g4 + (j16 >> 2);
+  const int fv = swz(vkey & 7);
+  uint32_t v_off[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    v_off[p] = LY::V_BASE + (ks * KW + vkey) * LY::V_PITCH +
+               16 * ((2 * p + ((j16 & 3) >> 1)) ^ fv) + 8 * (j16 & 1);
+
+  // ---- page copies: this wave's share ----
+  // latent rows k = wave + 4i: lane l copies chunk l ^ swz(k); k & 7 takes
+  // two values
+  uint32_t lat_voff[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) lat_voff[e] = 16 * (lane ^ swz((wave + NW * e) & 7));
+
+  for (int b = bs; b <= be; ++b) {
+    const int L = uniform(a.seqlens[b]);
+    const int npg = sched::seq_pages(L);
+    const int p0 = uniform(b == bs ? rec[sched::R_P_START] : 0);
+    const int p1 = uniform(b == be ? rec[sched::R_P_END] : npg);
+    const int s0 = uniform(a.slots[b]);
+    const int nslots = uniform(a.slots[b + 1]) - s0;
+
+    if (npg == 0) {
+      if ((b > bs || rec[sched::R_OWNS_FIRST]) && row_ok && ks == 0) {
+        uint16_t* o = a.out + ((size_t)b * TH + rho) * DV;
+        for (int cb = 0; cb < NCB; ++cb) *(u32x2*)(o + 16 * cb + 4 * g4) = u32x2{0u, 0u};
+        if (g4 == 0) a.lse[(size_t)b * TH + rho] = -INFINITY;
+      }
+      continue;
+    }
+    if (p0 >= p1) continue;
+    const int split = b == bs ? rec[sched::R_SPLIT0] : 0;
+    const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+
+    // copy page j of sequence b into buffer `buf`
+    auto issue_page = [&](int j, int buf) {
+      const int page = sload(uniform_ptr(bt + j));
+      const int nv = uniform(min(64, L - 64 * j));
+      const uint32_t dst = lds0 + buf * LY::TILE;
+      if constexpr (!GQA) {
+        const char* pbase = uniform_ptr((const char*)a.k + (size_t)page * (64 * 1152));
+#pragma unroll
+        for (int i = 0; i < 64 / NW; ++i) {
+          const int k = wave + NW * i;
+          const int kk = uniform(min(k, nv - 1));  // slots past the end repeat the last row
+          dma16(dst + k * 1024, uniform_ptr(pbase + kk * 1152), lat_voff[i & 1]);
+        }
+        // rope: 8 copies of 8 rows x 8 chunks; wave w takes copies w and w + 4
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int rr = wave + NW * i;
+          const int k = 8 * rr + (lane >> 3);
+          const uint32_t vo = min(k, nv - 1) * 1152 + 1024 + 16 * ((lane & 7) ^ swz(lane >> 3));
+          dma16(dst + LY::ROPE + rr * 1024, pbase, vo);
+        }
+      } else {
+        const uint32_t rstride = (uint32_t)a.G * 256;  // bytes between tokens
+        const size_t pg = ((size_t)page * 64 * a.G + g) * 256;
+        const char* kbase = uniform_ptr((const char*)a.k + pg);
+        const char* vbase = uniform_ptr((const char*)a.v + pg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ii = wave + NW * i;  // rows 4ii .. 4ii+3
+          const int k = 4 * ii + (lane >> 4);
+          const uint32_t vo = min(k, nv - 1) * rstride + 16 * ((lane & 15) ^ swz(k & 7));
+          dma16(dst + ii * 1024, kbase, vo);
+          dma16(dst + LY::V_BASE + ii * 1024, vbase, vo);
+        }
+      }
+    };
+
+    // queries of this lane's row, as B operands of the score MFMA
+    bf16x8 qf[KC];
+    {
+      const uint16_t* qrow = a.q + ((size_t)b * TH + rho) * D;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        u32x4 x = row_ok ? *(const u32x4*)(qrow + 32 * c + 8 * g4) : u32x4{0u, 0u, 0u, 0u};
+        qf[c] = __builtin_bit_cast(bf16x8, x);
+      }
+      // The page copies are inline asm the compiler does not count; consume
+      // q here so that its own wait for these loads sits before the page
+      // loop and not inside it.
+#pragma unroll
+      for (int c = 0; c < KC; ++c) asm volatile("" ::"v"(qf[c]));
+    }
+    const int vis = a.causal ? min(L - a.T + 1 + t, L) : L;
+
+    f32x4 o[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    issue_page(p0, 0);
+    for (int j = p0; j < p1; ++j) {
+      const int cur = (j - p0) & 1;
+      if (j + 1 < p1) {
+        issue_page(j + 1, cur ^ 1);
+        wait_vm<NDMA>();
+      } else {
+        wait_vm<0>();
+      }
+      barrier();
+      const uint32_t base = lds0 + cur * LY::TILE;
+
+      // S^T = K . Q^T, one 16-key block per kb; K fragments read two MFMA
+      // steps ahead
+      auto k_addr = [&](int st) -> uint32_t {
+        const int kb = st / KC, c = st % KC;
+        if (GQA || c < 16) return base + qk_off[c & 1] + kb * 16 * LY::K_PITCH + 128 * (c >> 1);
+        return base + rope_off[c & 1] + kb * 16 * LY::ROPE_PITCH;
+      };
+      constexpr int NQK = KB * KC;
+      f32x4 s[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 kf[3];
+      kf[0] = *LDS_PTR(const bf16x8, k_addr(0));
+      kf[1] = *LDS_PTR(const bf16x8, k_addr(1));
+#pragma unroll
+      for (int st = 0; st < NQK; ++st) {
+        if (st + 2 < NQK) kf[(st + 2) % 3] = *LDS_PTR(const bf16x8, k_addr(st + 2));
+        s[st / KC] = mfma16(kf[st % 3], qf[st % KC], s[st / KC]);
+        mem_fence_compiler();
+      }
+
+      // scale, mask, running max over this wave's keys
+      float tmax = -INFINITY;
+      const int kbase = 64 * j + ks * KW;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase + 16 * kb + 4 * g4 + i;
+          const float x = key < vis ? s[kb][i] * a.scale_log2 : -INFINITY;
+          s[kb][i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = max4groups(tmax);
+      // Lazy rescale: m is a per-row reference, not the exact running max.
+      // Weights are exp2(s - m) <= 2^RESCALE_SLACK; only when a page raises
+      // a row's max by more than that (or gives the row its first key) are
+      // l and O rescaled to the new reference. l and O always share the
+      // same reference, so the final O / l and m + log2(l) are exact.
+      const bool need = tmax > m + RESCALE_SLACK;
+      if (__any(need)) {
+        // rows that do not need it keep alpha = 1 (a row that has seen no
+        // key yet has m = -inf, and exp2(m - m) would be NaN)
+        const float alpha = need ? fast_exp2(m - tmax) : 1.f;  // 0 when m = -inf
+        l *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+        m = need ? tmax : m;
+      }
+      const float m_use = m == -INFINITY ? 0.f : m;
+      float psum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(s[kb][i] - m_use);
+          s[kb][i] = p;
+          psum += p;
+        }
+      l += sum4groups(psum);
+
+      // O^T += V^T . P^T
+      if constexpr (KW >= 32) {
+        // K step c covers this wave's keys 32c .. 32c+31; slot i of lane l
+        // holds key 32c + 16(i/4) + 4(l/16) + i%4 = score block 2c + i/4,
+        // register i%4.
+        constexpr int PC = KW / 32;
+        bf16x8 pf[PC];
+#pragma unroll
+        for (int c = 0; c < PC; ++c) {
+          u32x4 x;
+          x[0] = pack_bf16x2(s[2 * c][0], s[2 * c][1]);
+          x[1] = pack_bf16x2(s[2 * c][2], s[2 * c][3]);
+          x[2] = pack_bf16x2(s[2 * c + 1][0], s[2 * c + 1][1]);
+          x[3] = pack_bf16x2(s[2 * c + 1][2], s[2 * c + 1][3]);
+          pf[c] = __builtin_bit_cast(bf16x8, x);
+        }
+        auto v_frag = [&](int st) -> bf16x8 {
+          const int cb = st / PC, c = st % PC;
+          const uint32_t a0 = base + v_off[cb & 3] + (32 * c) * LY::V_PITCH + 128 * (cb >> 2);
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
+          const bf16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * LY::V_PITCH));
+          return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        constexpr int NST = NCB * PC;
+        bf16x8 vf[3];
+        vf[0] = v_frag(0);
+        vf[1] = v_frag(1);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          if (st + 2 < NST) vf[(st + 2) % 3] = v_frag(st + 2);
+          o[st / PC] = mfma16(vf[st % 3], pf[st % PC], o[st / PC]);
+          mem_fence_compiler();
+        }
+      } else {
+        // 16 keys per wave: 16x16x16 MFMA, slot i of lane l holds key
+        // 4(l/16) + i, exactly score register i.
+        u32x2 px;
+        px[0] = pack_bf16x2(s[0][0], s[0][1]);
+        px[1] = pack_bf16x2(s[0][2], s[0][3]);
+        const bf16x4 pf = __builtin_bit_cast(bf16x4, px);
+        auto v_frag = [&](int cb) -> bf16x4 {
+          const uint32_t a0 = base + v_off[cb & 3] + 128 * (cb >> 2);
+          return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
+        };
+        bf16x4 vf[3];
+        vf[0] = v_frag(0);
+        vf[1] = v_frag(1);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          if (cb + 2 < NCB) vf[(cb + 2) % 3] = v_frag(cb + 2);
+          o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[cb % 3], pf, o[cb], 0, 0, 0);
+          mem_fence_compiler();
+        }
+      }
+      barrier();  // every wave is done with this buffer before it is refilled
+    }
+
+    // merge the key parts of each row group through LDS (page buffers are
+    // free: every copy has landed and every wave has passed the last barrier)
+    if constexpr (KS > 1) {
+      float* red = (float*)lds;  // [KS-1][R][NCB*4 + 2][64] floats
+      constexpr int PER = NCB * 4 + 2;
+      if (ks > 0) {
+        float* my = red + ((ks - 1) * R + rg) * PER * 64 + lane;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) my[(cb * 4 + i) * 64] = o[cb][i];
+        my[(NCB * 4) * 64] = m;
+        my[(NCB * 4 + 1) * 64] = l;
+      }
+      __syncthreads();
+      if (ks == 0) {
+#pragma unroll
+        for (int part = 1; part < KS; ++part) {
+          const float* ot = red + ((part - 1) * R + rg) * PER * 64 + lane;
+          const float m2 = ot[(NCB * 4) * 64], l2 = ot[(NCB * 4 + 1) * 64];
+          const float mm = fmaxf(m, m2);
+          const float mu = mm == -INFINITY ? 0.f : mm;
+          const float a1 = fast_exp2(m - mu), a2 = fast_exp2(m2 - mu);
+          l = a1 * l + a2 * l2;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[cb][i] = a1 * o[cb][i] + a2 * ot[(cb * 4 + i) * 64];
+          m = mm;
+        }
+      }
+      __syncthreads();  // the buffers are refilled by the next sequence
+    }
+
+    // epilogue: normalise; lane l holds dv = 16cb + 4(l/16) + i
+    if (row_ok && ks == 0) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lse_v = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
+    if (nslots == 0) {
+      uint16_t* orow = a.out + ((size_t)b * TH + rho) * DV;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        u32x2 x;
+        x[0] = pack_bf16x2(o[cb][0] * inv, o[cb][1] * inv);
+        x[1] = pack_bf16x2(o[cb][2] * inv, o[cb][3] * inv);
+        *(u32x2*)(orow + 16 * cb + 4 * g4) = x;
+      }
+      if (g4 == 0) a.lse[(size_t)b * TH + rho] = lse_v;
+    } else {
+      const size_t slot = (size_t)(s0 + split);
+      float* prow = a.part_o + (slot * TH + rho) * DV;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) *(f32x4*)(prow + 16 * cb + 4 * g4) = o[cb] * inv;
+      if (g4 == 0) a.part_lse[slot * TH + rho] = lse_v;
+    }
+    }
+  }
+}
+
+template <int R, bool GQA>
+static hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((decode_kernel<R, GQA>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_kernel(const DecodeArgs& a, int row_groups, bool gqa, int grid,
+                                hipStream_t st) {
+  if (!gqa) {
+    switch (row_groups) {
+      case 1: return launch_decode<1, false>(a, grid, st);
+      case 2: return launch_decode<2, false>(a, grid, st);
+      case 4: return launch_decode<4, false>(a, grid, st);
+    }
+  } else {
+    switch (row_groups) {
+      case 1: return launch_decode<1, true>(a, grid, st);
+      case 2: return launch_decode<2, true>(a, grid, st);
+      case 4: return launch_decode<4, true>(a, grid, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mla

@@ -1,0 +1,108 @@
+// Split-KV schedule: how the pages of a variable-length batch are spread
+// over a fixed set of workgroups ("workers").
+//
+// FlashAttention (KO), section "FlashAttention-2 (2023)", credits better
+// parallelism and work partitioning across the GPU; the FlashMLA blog
+// ("기술 기반") asks for efficient variable-length handling. Here the work
+// of sequence b is FIXED_UNITS overhead units (loading its queries, writing
+// its result) followed by one unit per 64-token page; the units of the whole
+// batch are concatenated and cut into num_workers equal contiguous ranges of
+// `chunk` units. A sequence whose pages fall into several ranges is split;
+// each piece writes a partial result that a log-sum-exp merge finishes.
+//
+// Every function here is plain arithmetic usable on the host (for the
+// host-side checker) and on the device (for the plan kernel).
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define SCHED_HD __host__ __device__ inline
+#else
+#define SCHED_HD inline
+#endif
+
+namespace sched {
+
+constexpr int PAGE = 64;
+constexpr int FIXED_UNITS = 2;
+constexpr int REC = 8;  // int32 per worker record
+
+// Worker record layout (int32 x REC).
+enum : int {
+  R_B_START = 0,    // first sequence touched
+  R_P_START = 1,    // first page of R_B_START
+  R_B_END = 2,      // last sequence touched (inclusive); < R_B_START when idle
+  R_P_END = 3,      // one past the last page of R_B_END
+  R_SPLIT0 = 4,     // split index of this worker's piece of R_B_START
+  R_OWNS_FIRST = 5, // 1 if this worker holds the first unit of R_B_START
+  R_LO = 6,         // unit range [lo, hi)
+  R_HI = 7
+};
+
+SCHED_HD int seq_pages(int32_t L) { return L > 0 ? (L + PAGE - 1) / PAGE : 0; }
+SCHED_HD int seq_units(int32_t L) { return seq_pages(L) + FIXED_UNITS; }
+
+// Largest b in [0, B) with prefix[b] <= u (prefix strictly increasing,
+// prefix[0] = 0 <= u).
+SCHED_HD int find_seq(const int32_t* prefix, int B, int64_t u) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= u) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+SCHED_HD int chunk_units(int32_t total_units, int W) {
+  int c = (total_units + W - 1) / W;
+  return c > 0 ? c : 1;
+}
+
+// Record of worker w. prefix has B + 1 entries (prefix[B] = total units).
+SCHED_HD void worker_record(int w, int W, const int32_t* prefix, const int32_t* seqlens,
+                            int B, int32_t* rec) {
+  const int32_t C = prefix[B];
+  const int chunk = chunk_units(C, W);
+  const int64_t lo = (int64_t)w * chunk;
+  if (lo >= C) {
+    rec[R_B_START] = 0; rec[R_P_START] = 0; rec[R_B_END] = -1; rec[R_P_END] = 0;
+    rec[R_SPLIT0] = 0; rec[R_OWNS_FIRST] = 0; rec[R_LO] = C; rec[R_HI] = C;
+    return;
+  }
+  const int64_t hi = (lo + chunk < C) ? lo + chunk : C;
+  const int bs = find_seq(prefix, B, lo);
+  const int be = find_seq(prefix, B, hi - 1);
+  int64_t ps = lo - prefix[bs] - FIXED_UNITS;
+  if (ps < 0) ps = 0;
+  const int ne = seq_pages(seqlens[be]);
+  int64_t pe = hi - prefix[be] - FIXED_UNITS;
+  if (pe < 0) pe = 0;
+  if (pe > ne) pe = ne;
+  const int first_w = (prefix[bs] + FIXED_UNITS) / chunk;
+  rec[R_B_START] = bs;
+  rec[R_P_START] = (int32_t)ps;
+  rec[R_B_END] = be;
+  rec[R_P_END] = (int32_t)pe;
+  rec[R_SPLIT0] = w > first_w ? w - first_w : 0;
+  rec[R_OWNS_FIRST] = prefix[bs] == lo ? 1 : 0;
+  rec[R_LO] = (int32_t)lo;
+  rec[R_HI] = (int32_t)hi;
+}
+
+// Number of workers that process pages of sequence b (1 for an empty one).
+SCHED_HD int seq_split_count(int b, int W, const int32_t* prefix, const int32_t* seqlens, int B) {
+  if (seq_pages(seqlens[b]) == 0) return 1;
+  const int chunk = chunk_units(prefix[B], W);
+  const int first = (prefix[b] + FIXED_UNITS) / chunk;
+  const int last = (prefix[b + 1] - 1) / chunk;
+  return last - first + 1;
+}
+
+// Partial-result slots of sequence b: none when one worker finishes it.
+SCHED_HD int seq_slots(int b, int W, const int32_t* prefix, const int32_t* seqlens, int B) {
+  const int n = seq_split_count(b, W, prefix, seqlens, B);
+  return n > 1 ? n : 0;
+}
+
+}  // namespace sched

@@ -365,3 +365,28 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     monkeypatch.setattr(A, "scale_as_received", lambda s: 1.0)
     bad = run(A.attend_two_pass, d)
     assert not np.allclose(bad[1], brute[1])
+
+
+# ------------------------------------------------------------- tolerance
+def test_tolerance_checker():
+    from oracle import compare, bf16_step
+    assert bf16_step(np.array([1.0]))[0] == 2.0 ** -7
+    assert bf16_step(np.array([5.0]))[0] == 2.0 ** -5
+    ref = np.zeros((2, 101))
+    ref[0, :100], ref[0, 100] = 1.0, 5.0
+    lse_ref = np.array([0.5, -np.inf])
+    got = ref.copy()
+    got[0, 100] = 5.03125                      # one bf16 step above 5: allowed
+    ok = compare(got, np.array([0.5004, -np.inf]), ref, lse_ref)
+    assert ok["ok"] and ok["ulp_exceptions"] == 1
+    got = ref.copy()
+    got[0, 0] = 1.02                           # 0.02 off at 1.0: more than a bf16 step
+    assert not compare(got, np.array([0.5, -np.inf]), ref, lse_ref)["ok"]
+    got = ref.copy()
+    got[1, 3] = 1e-3                           # an empty row must be exactly zero
+    bad = compare(got, np.array([0.5, -np.inf]), ref, lse_ref)
+    assert not bad["ok"] and not bad["empty_ok"]
+    assert not compare(ref, np.array([0.502, -np.inf]), ref, lse_ref)["ok"]
+    got = ref.copy()
+    got[0, :100] = 1.0078125                   # every element one step off: rel-L2 fails
+    assert not compare(got, np.array([0.5, -np.inf]), ref, lse_ref)["ok"]

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path through the C interface against the fp64 oracle
+on the same seeded inputs (max-abs 1e-2 with a one-bf16-step allowance,
+rel-L2 5e-3, LSE 1e-3), plus properties that hold at any size."""
+import numpy as np
+import pytest
+
+from workloads import CONFIGS
+from gpu_helpers import check, inputs, log, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_kv_03_amd as lib
+    lib._lib.lib()  # fail loudly if the library is missing
+    return torch.device("cuda:0")
+
+
+# ------------------------------------------------------------ small shapes
+def _mla(B, T, H, Ls, causal, **kw):
+    return CONFIGS[3].with_(batch=B, s_q=T, h_q=H, causal=causal, seqlen_rule="fixed",
+                            seqlens_fixed=tuple(Ls), **kw)
+
+
+def _gqa(B, T, H, G, Ls, causal=False):
+    return CONFIGS[5].with_(batch=B, s_q=T, h_q=H, h_kv=G, causal=causal, seqlen_rule="fixed",
+                            seqlens_fixed=tuple(Ls))
+
+
+RAGGED = (0, 1, 2, 63, 64, 65, 127, 200, 640, 1000)
+SMALL = {
+    "mla_h8_t1": _mla(10, 1, 8, RAGGED, False),
+    "mla_h16_t1": _mla(10, 1, 16, RAGGED, False),
+    "mla_h32_t1": _mla(10, 1, 32, RAGGED, False),
+    "mla_h64_t1": _mla(10, 1, 64, RAGGED, False),
+    "mla_h128_t1": _mla(10, 1, 128, RAGGED, False),
+    "mla_h128_t2_causal": _mla(10, 2, 128, RAGGED, True),
+    "mla_h16_t3_causal": _mla(10, 3, 16, RAGGED, True),
+    # 40 and 8 heads per token: one wave's 16 rows mix query tokens, so under
+    # causal masking some rows of a wave see a key while others see none yet
+    "mla_h40_t2_causal": _mla(10, 2, 40, RAGGED, True),
+    "mla_h128_t1_kvhalf": _mla(4, 1, 128, (4096, 100, 3000, 1), False, kv_std=0.5),
+    "gqa_h128_g8": _gqa(10, 1, 128, 8, RAGGED),
+    "gqa_h16_g2": _gqa(10, 1, 16, 2, RAGGED),
+    "gqa_h8_g8": _gqa(10, 1, 8, 8, RAGGED),
+    "gqa_h32_g4_t2_causal": _gqa(10, 2, 32, 4, RAGGED, True),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_shapes_match_oracle(dev, name):
+    cfg = SMALL[name]
+    d = inputs(cfg, seed=11)
+    log(f"[case] {name} seqlens={list(d['cache_seqlens'])}")
+    out, lse = run_gpu(d, to_device(d, dev))
+    ref_out, ref_lse = run_oracle(d)
+    check(out, lse, ref_out, ref_lse, name)
+
+
+# ------------------------------------------------------- the five configs
+def _sample(cfg, d, k=6):
+    """Sequences to check against the oracle at full size: the shortest,
+    the longest, and a seeded random pick."""
+    L = d["cache_seqlens"]
+    rng = np.random.default_rng(1234)
+    pick = {int(np.argmin(L)), int(np.argmax(L))}
+    pick |= set(int(x) for x in rng.choice(cfg.batch, size=min(k, cfg.batch), replace=False))
+    ones = np.nonzero(L == 1)[0]
+    pick |= set(int(x) for x in ones[:2])
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_config_matches_oracle(dev, idx):
+    import torch
+    cfg = CONFIGS[idx]
+    log(f"[case] config {idx} {cfg.name}: generating inputs")
+    d = inputs(cfg)
+    t = to_device(d, dev)
+    out, lse = run_gpu(d, t)
+    assert np.isfinite(out).all(), "non-finite output"
+    L = d["cache_seqlens"]
+    empty_rows = ~np.isfinite(lse)
+    # at any size: rows with keys have finite lse; rows without are exactly empty
+    if not cfg.causal:
+        assert np.array_equal(empty_rows.any(axis=(1, 2)), L == 0)
+    b_idx = list(range(cfg.batch)) if idx == 1 else _sample(cfg, d)
+    log(f"[case] config {idx}: oracle on sequences {b_idx}")
+    ref_out, ref_lse = run_oracle(d, b_idx)
+    check(out[b_idx], lse[b_idx], ref_out, ref_lse, f"config {idx} ({cfg.name})")
+    del t
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------- properties
+@pytest.mark.parametrize("name", ["mla_h128_t2_causal", "mla_h16_t1", "gqa_h128_g8"])
+def test_nan_in_page_tails_and_pads_is_never_read(dev, name):
+    cfg = SMALL[name]
+    clean = inputs(cfg, seed=5)
+    dirty = inputs(cfg, seed=5, poison=True)
+    o1, l1 = run_gpu(clean, to_device(clean, dev))
+    o2, l2 = run_gpu(dirty, to_device(dirty, dev))
+    assert np.isfinite(o2).all()
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["mla_h128_t2_causal", "gqa_h32_g4_t2_causal"])
+def test_page_permutation_and_rerun_are_bitwise_equal(dev, name):
+    cfg = SMALL[name]
+    d = inputs(cfg, seed=6)
+    o1, l1 = run_gpu(d, to_device(d, dev))
+    o1b, l1b = run_gpu(d, to_device(d, dev))
+    assert np.array_equal(o1, o1b) and np.array_equal(l1, l1b), "not deterministic"
+    rng = np.random.default_rng(2)
+    perm = rng.permutation(d["num_pages"])
+    bt = d["block_table"].copy()
+    bt[bt >= 0] = perm[bt[bt >= 0]]
+    d2 = dict(d, block_table=bt)
+    for key in ("kv", "k", "v"):
+        if key in d:
+            moved = np.empty_like(d[key])
+            moved[perm] = d[key]
+            d2[key] = moved
+    o2, l2 = run_gpu(d2, to_device(d2, dev))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_split_count_does_not_change_the_result(dev):
+    # one long sequence alone is cut over every worker; in a crowded batch
+    # it is cut fewer times
+    cfg_alone = _mla(1, 2, 128, (5000,), True)
+    cfg_batch = _mla(40, 2, 128, (5000,) + (4000,) * 39, True)
+    alone = inputs(cfg_alone, seed=8)
+    crowd = inputs(cfg_batch, seed=8)
+    # put the same sequence (q and pages) in slot 0 of the crowded batch
+    n0 = (5000 + 63) // 64
+    crowd["q"][0] = alone["q"][0]
+    crowd["kv"][crowd["block_table"][0, :n0]] = alone["kv"][alone["block_table"][0, :n0]]
+    o1, l1 = run_gpu(alone, to_device(alone, dev))
+    o2, l2 = run_gpu(crowd, to_device(crowd, dev))
+    ref_out, ref_lse = run_oracle(alone)
+    check(o1, l1, ref_out, ref_lse, "alone")
+    check(o2[:1], l2[:1], ref_out, ref_lse, "in a batch")
+
+
+def test_causal_tokens_reduce_to_single_token_decode(dev):
+    cfg = SMALL["mla_h128_t2_causal"]
+    d = inputs(cfg, seed=9)
+    out, lse = run_gpu(d, to_device(d, dev))
+    L = d["cache_seqlens"]
+    one = cfg.with_(s_q=1, causal=False)
+    for shift, tok in ((0, 1), (1, 0)):
+        d1 = dict(d, cfg=one, q=np.ascontiguousarray(d["q"][:, tok:tok + 1]),
+                  cache_seqlens=np.maximum(L - shift, 0).astype(np.int32))
+        o1, l1 = run_gpu(d1, to_device(d1, dev))
+        check(out[:, tok:tok + 1], lse[:, tok:tok + 1], o1, l1, f"token {tok} vs single")
+
+
+def test_empty_batch_is_a_no_op(dev):
+    import torch
+    import mla_paged_kv_03_amd as lib
+    q = torch.zeros(0, 1, 16, 576, dtype=torch.bfloat16, device=dev)
+    kv = torch.zeros(1, 64, 1, 576, dtype=torch.bfloat16, device=dev)
+    bt = torch.zeros(0, 1, dtype=torch.int32, device=dev)
+    sl = torch.zeros(0, dtype=torch.int32, device=dev)
+    out, lse = lib.mla_decode(q, kv, bt, sl, 0.1, False)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 1, 16, 512)
+
+
+def test_workspace_too_small_is_reported(dev):
+    import torch
+    import mla_paged_kv_03_amd as lib
+    cfg = SMALL["mla_h16_t1"]
+    d = inputs(cfg, seed=1)
+    t = to_device(d, dev)
+    plan = lib.mla_decode_plan(t["cache_seqlens"], 1, 16)
+    plan.workspace = plan.workspace[:16]
+    with pytest.raises(lib.DecodeError) as e:
+        lib.mla_decode(t["q"], t["kv"], t["block_table"], t["cache_seqlens"], cfg.scale, False,
+                       plan=plan)
+    assert e.value.code == -4
+
+
+def test_device_plan_equals_host_plan(dev):
+    import torch
+    import mla_paged_kv_03_amd as lib
+    for Ls, T, H, G, dv in [((64, 200), 1, 8, 1, 512),
+                            (tuple(np.random.default_rng(3).integers(0, 16385, 128)), 2, 128, 1, 512),
+                            ((8192,) * 256, 1, 16, 1, 512), ((100, 0, 70000), 1, 128, 8, 128)]:
+        sl = torch.tensor(Ls, dtype=torch.int32, device=dev)
+        plan = lib.mla_decode_plan(sl, T, H, G, dv)
+        torch.cuda.synchronize()
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        meta, splits, info = lib.mla_decode_plan_host(Ls, T, H, G, dv, num_cus=cus)
+        assert np.array_equal(plan.sched_metadata.cpu().numpy(), meta)
+        assert np.array_equal(plan.num_splits.cpu().numpy(), splits)
+
+
+def test_attn_combine_matches_oracle_combine(dev):
+    import torch
+    import oracle
+    import mla_paged_kv_03_amd as lib
+    rng = np.random.default_rng(4)
+    B, R, dv = 3, 5, 64
+    counts = [3, 0, 2]
+    slots = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    S = int(slots[-1])
+    po = rng.standard_normal((S, R, dv)).astype(np.float32)
+    pl = (rng.standard_normal((S, R)) * 3).astype(np.float32)
+    pl[1, 2] = -np.inf                       # a part that saw no key
+    pl[3:5, 4] = -np.inf                     # a row with no key at all
+    po[3:5, 4] = 0.0
+    out, lse = lib.attn_combine(torch.from_numpy(po).to(dev), torch.from_numpy(pl).to(dev),
+                                torch.from_numpy(slots).to(dev))
+    torch.cuda.synchronize()
+    out = out.float().cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    for b in range(B):
+        if counts[b] == 0:
+            assert (out[b] == 0).all() and (lse[b] == -np.inf).all()  # untouched
+            continue
+        parts = [(po[s].astype(np.float64), pl[s].astype(np.float64))
+                 for s in range(slots[b], slots[b + 1])]
+        ro, rl = oracle.combine(parts)
+        check(out[b], lse[b], ro, rl, f"combine b={b}")
