@@ -71,9 +71,10 @@ def stored_traffic():
     return int(m1.group(1)) if m2.group(1) == cur else None
 
 
-def cpu_baseline(d, budget_s=20.0):
-    """The oracle as it stands, on the host cores, over as many whole
-    sequences of the workload as fit in about budget_s seconds."""
+def cpu_baseline(d, budget_s=10.0):
+    """The oracle as it stands, on the host cores, over whole sequences of
+    the workload, in order and wrapping around, until about budget_s seconds
+    of work are done (at least one sequence)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -82,8 +83,8 @@ def cpu_baseline(d, budget_s=20.0):
         threads = len(os.sched_getaffinity(0))
     cfg = d["cfg"]
     done, t0 = 0, time.perf_counter()
-    while done < cfg.batch and time.perf_counter() - t0 < budget_s:
-        idx = [done]
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        idx = [done % cfg.batch]
         q = d["q"][idx]
         bt = d["block_table"][idx]
         L = d["cache_seqlens"][idx]
@@ -95,8 +96,9 @@ def cpu_baseline(d, budget_s=20.0):
     dt = time.perf_counter() - t0
     return {"value": done * cfg.s_q / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {cfg.batch} sequences of the same workload "
-                      f"({done * cfg.s_q} query tokens, {dt:.1f} s, fp64 numpy)"}
+            "sample": f"{done} sequences of the same workload taken in order "
+                      f"(batch {cfg.batch}; {done * cfg.s_q} query tokens, {dt:.1f} s, "
+                      f"fp64 numpy)"}
 
 
 def main():
@@ -107,6 +109,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs the decode on one GPU only; "
@@ -114,6 +119,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 3}), flush=True)
+        return
     import mla_paged_kv_03_amd as lib
     from mla_paged_kv_03_amd import _lib
     from workloads import CONFIGS, make_inputs
@@ -174,22 +189,35 @@ def main():
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     # timed region: whole steps, and the decode kernel alone via the
-    # library's event hook (events recorded on the kernel's own stream)
+    # library's event hook (HIP events recorded on the kernel's own stream)
+    hip = ctypes.CDLL("libamdhip64.so")
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    ev = []
+    for _ in range(2 * K):
+        h = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        ev.append(h)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for i in range(K):
-        lib.profile_events(ev[i][0], ev[i][1])
+        L.mla_profile_events(ev[2 * i], ev[2 * i + 1])
         step(i)
     t_end.record()
     torch.cuda.synchronize()
-    lib.profile_events(None, None)
+    L.mla_profile_events(None, None)
     ms_step = t_start.elapsed_time(t_end) / K
-    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    kern_ms = []
+    for i in range(K):
+        ms = ctypes.c_float()
+        if hip.hipEventElapsedTime(ctypes.byref(ms), ev[2 * i], ev[2 * i + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        kern_ms.append(ms.value)
+    for h in ev:
+        hip.hipEventDestroy(h)
+    kern_ms = np.array(kern_ms)
     kern_avg = float(kern_ms.mean())
 
     # same loop without the event hook: the step rate with nothing extra

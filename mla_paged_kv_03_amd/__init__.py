@@ -195,8 +195,9 @@ def mla_decode_plan_host(seqlens, s_q, h_q, h_kv=1, head_dim_v=MLA_DV, num_cus=2
 
 
 def profile_events(start=None, stop=None):
-    """Record `start` / `stop` (torch.cuda.Event) around the main decode
-    kernel of every following decode call on its stream; None clears."""
-    _lib.lib().mla_profile_events(
-        ctypes.c_void_p(start.cuda_event) if start is not None else None,
-        ctypes.c_void_p(stop.cuda_event) if stop is not None else None)
+    """Record the HIP events `start` / `stop` (raw hipEvent_t handles, as
+    ints or ctypes.c_void_p) around the main decode kernel of every following
+    decode call on its stream; None clears."""
+    conv = lambda e: None if e is None else (e if isinstance(e, ctypes.c_void_p)
+                                             else ctypes.c_void_p(int(e)))
+    _lib.lib().mla_profile_events(conv(start), conv(stop))

@@ -87,8 +87,12 @@ struct Layout<true> {
 // LDS byte lds + 16 * l. Issued from inline asm so that the compiler does not
 // add its own conservative wait on the asynchronous LDS write; the kernel
 // waits with explicit vmcnt counts.
+// The compiler does not insert hazard wait states inside inline asm, so the
+// block carries its own: a VALU write of an SGPR (readfirstlane of the base)
+// needs 5 wait states before a vector memory instruction reads that SGPR, and
+// an SALU write of M0 needs 1 before an LDS DMA reads M0.
 __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(lds), "v"(voff), "s"(sbase)
                : "memory", "m0");

@@ -228,3 +228,43 @@ def test_attn_combine_matches_oracle_combine(dev):
                  for s in range(slots[b], slots[b + 1])]
         ro, rl = oracle.combine(parts)
         check(out[b], lse[b], ro, rl, f"combine b={b}")
+
+
+def _climbing_scores(d, cfg, period=5, step=18.0, seed=7):
+    """Give every query head the same q, and page j keys close to
+    alpha_j * q with alpha_j chosen so the log2-domain score of page j is
+    about step * (j mod period): within each run of `period` pages every
+    row's scores climb past the previous page's by `step`."""
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    q0 = rng.standard_normal(cfg.d_qk).astype(np.float32)
+    d["q"][:] = f32_to_bf16_bits(np.broadcast_to(q0, d["q"].shape))
+    kname = "kv" if cfg.kind == "mla" else "k"
+    sigma = float(np.float32(cfg.scale)) * 1.4426950408889634
+    per_unit = float(q0 @ q0) * sigma
+    for b in range(cfg.batch):
+        n = (int(d["cache_seqlens"][b]) + 63) // 64
+        for j in range(n):
+            alpha = step * (j % period) / per_unit
+            noise = 0.05 * rng.standard_normal((64,) + d[kname].shape[2:]).astype(np.float32)
+            d[kname][d["block_table"][b, j]] = f32_to_bf16_bits(alpha * q0 + noise)
+
+
+@pytest.mark.parametrize("kind", ["mla", "gqa"])
+def test_scores_climbing_past_the_slack_rescale_the_running_sums(dev, kind):
+    """Scores that rise by more than the kernel's rescale slack from one page
+    to the next force the online-softmax rescale of O and l on page after
+    page; each worker here owns several consecutive pages (the batch has far
+    more pages than workers), so every worker rescales mid-range."""
+    import mla_paged_kv_03_amd as lib
+    Ls = (64 * 300, 64 * 280 + 17, 64 * 300, 64 * 290)
+    cfg = (_mla(4, 1, 16, Ls, False) if kind == "mla" else _gqa(4, 1, 16, 2, Ls))
+    d = inputs(cfg, seed=12)
+    _climbing_scores(d, cfg)
+    t = to_device(d, dev)
+    plan = lib.mla_decode_plan(t["cache_seqlens"], cfg.s_q, cfg.h_q, cfg.h_kv, cfg.d_v)
+    pages = int(((d["cache_seqlens"] + 63) // 64).sum())
+    assert pages > 2 * plan.info.num_workers  # several pages per worker
+    out, lse = run_gpu(d, t, plan=plan)
+    ref_out, ref_lse = run_oracle(d)
+    check(out, lse, ref_out, ref_lse, f"climbing scores ({kind})")
