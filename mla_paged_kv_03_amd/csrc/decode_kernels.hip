@@ -54,33 +54,39 @@ __device__ __forceinline__ void decode_block_id(int bid, int W, int RB, int& w, 
   }
 }
 
-// LDS page layouts (bytes). Row k of a region with P bytes per row keeps its
-// 16-byte chunk c at k * P + 16 * (c ^ swz(k)).
+// LDS page layouts (bytes). Row k of a page keeps its 16-byte chunk c at
+// k * PITCH + 16 * (c ^ row_xor(k)). Measured on gfx950 (whose LDS serves
+// 256 bytes per clock), these two choices let the K-operand reads (16 rows x
+// 16 bytes per 16-lane group) run at the full LDS rate and the transposed V
+// reads (4 rows x 32 bytes per group) at their best rate; a 3-bit XOR over
+// 1 KiB rows ran both at about half of that.
 template <bool GQA>
 struct Layout;
 
-// Latent cache: 576-wide rows split as columns 0..511 (latent, which is also
-// V) and 512..575 (rope).
+// Latent cache: a page is copied as it lies in HBM, 64 rows of 1152 bytes:
+// columns 0..511 (latent, which is also V) in chunks 0..63, the rope columns
+// 512..575 in chunks 64..71. The XOR (row & 7) stays inside aligned groups of
+// 8 chunks, so the rope stays in chunks 64..71.
 template <>
 struct Layout<false> {
   static constexpr int D = 576, DV = 512;
-  static constexpr int TILE = 64 * 1152;  // one page
-  static constexpr int K_PITCH = 1024;    // latent region: 64 chunks per row
-  static constexpr int ROPE = 65536;      // rope region: 8 chunks per row
-  static constexpr int ROPE_PITCH = 128;
-  static constexpr int V_BASE = 0, V_PITCH = 1024;
+  static constexpr int PITCH = 1152;
+  static constexpr int TILE = 64 * PITCH;  // one page
+  static constexpr int V_BASE = 0;
   static constexpr int DMA_PER_TILE = 72;  // 1 KiB per instruction
+  static __device__ __forceinline__ int row_xor(int k) { return k & 7; }
 };
 
-// GQA: separate 128-wide K and V rows of one KV head.
+// GQA: separate 128-wide K and V rows (256 bytes, 16 chunks) of one KV head;
+// the XOR 2 (k & 7) stays inside the row.
 template <>
 struct Layout<true> {
   static constexpr int D = 128, DV = 128;
-  static constexpr int TILE = 2 * 64 * 256;
-  static constexpr int K_PITCH = 256;
-  static constexpr int ROPE = 0, ROPE_PITCH = 0;
-  static constexpr int V_BASE = 64 * 256, V_PITCH = 256;
+  static constexpr int PITCH = 256;
+  static constexpr int TILE = 2 * 64 * PITCH;
+  static constexpr int V_BASE = 64 * PITCH;
   static constexpr int DMA_PER_TILE = 32;
+  static __device__ __forceinline__ int row_xor(int k) { return (k & 7) << 1; }
 };
 
 // Issue one 1 KiB HBM -> LDS copy: lane l's 16 bytes at sbase + voff land at
@@ -188,31 +194,30 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int TH = a.T * a.H;
 
   // ---- per-lane LDS offsets (bytes, relative to a page buffer) ----
-  // score operand: key ks*KW + 16kb + n, 16-byte chunk 4c + g4 of the K row
-  const int fn = swz(n & 7);
-  uint32_t qk_off[2], rope_off[2];
+  // Score operand: key ks*KW + 16kb + n, K step c covers columns 32c .. 32c+31,
+  // of which this lane reads chunk 4c + g4. MLA: the XOR (< 8) leaves the
+  // 8-chunk group alone, so two offsets (c even / odd) plus 128 (c >> 1)
+  // cover all 18 steps, rope included. GQA: the 4-bit XOR reaches across the
+  // group, so each of the 4 steps has its own offset.
+  constexpr int NQO = GQA ? 4 : 2;
+  const int xn = LY::row_xor(n);
+  uint32_t qk_off[NQO];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    qk_off[p] = (ks * KW + n) * LY::K_PITCH + 16 * ((4 * p + g4) ^ fn);
-    rope_off[p] = LY::ROPE + (ks * KW + n) * LY::ROPE_PITCH + 16 * ((4 * p + g4) ^ fn);
-  }
+  for (int q = 0; q < NQO; ++q)
+    qk_off[q] = (ks * KW + n) * LY::PITCH + 16 * ((4 * q + g4) ^ xn);
   // V^T operand by transposed reads: 16-lane group g4 reads keys
-  // 4*g4 + (j>>2) (+ a multiple of 16) at columns 16cb + 4(j&3) .. +3
+  // 4*g4 + (j>>2) (+ a multiple of 16) at columns 16cb + 4(j&3) .. +3, i.e.
+  // chunk 2cb + (j&3)/2; MLA needs 4 offsets (cb & 3) plus 128 (cb >> 2),
+  // GQA one per column block.
+  constexpr int NVO = GQA ? 8 : 4;
   const int j16 = lane & 15;
   const int vkey = 4 * g4 + (j16 >> 2);
-  const int fv = swz(vkey & 7);
-  uint32_t v_off[4];
+  const int xv = LY::row_xor(vkey);
+  uint32_t v_off[NVO];
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
-    v_off[p] = LY::V_BASE + (ks * KW + vkey) * LY::V_PITCH +
-               16 * ((2 * p + ((j16 & 3) >> 1)) ^ fv) + 8 * (j16 & 1);
-
-  // ---- page copies: this wave's share ----
-  // latent rows k = wave + 4i: lane l copies chunk l ^ swz(k); k & 7 takes
-  // two values
-  uint32_t lat_voff[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) lat_voff[e] = 16 * (lane ^ swz((wave + NW * e) & 7));
+  for (int q = 0; q < NVO; ++q)
+    v_off[q] = LY::V_BASE + (ks * KW + vkey) * LY::PITCH +
+               16 * ((2 * q + ((j16 & 3) >> 1)) ^ xv) + 8 * (j16 & 1);
 
   for (int b = bs; b <= be; ++b) {
     const int L = uniform(a.seqlens[b]);
@@ -240,20 +245,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const int nv = uniform(min(64, L - 64 * j));
       const uint32_t dst = lds0 + buf * LY::TILE;
       if constexpr (!GQA) {
-        const char* pbase = uniform_ptr((const char*)a.k + (size_t)page * (64 * 1152));
+        // the page is one contiguous 72 KiB block in HBM and in LDS: copy i
+        // fills LDS bytes 1024i .. 1024i+1023, 16-byte unit u = 64i + lane,
+        // i.e. chunk x of row r; rows past the sequence end repeat its last
+        // row (finite data that the mask gives weight 0)
+        const char* pbase = uniform_ptr((const char*)a.k + (size_t)page * LY::TILE);
 #pragma unroll
-        for (int i = 0; i < 64 / NW; ++i) {
-          const int k = wave + NW * i;
-          const int kk = uniform(min(k, nv - 1));  // slots past the end repeat the last row
-          dma16(dst + k * 1024, uniform_ptr(pbase + kk * 1152), lat_voff[i & 1]);
-        }
-        // rope: 8 copies of 8 rows x 8 chunks; wave w takes copies w and w + 4
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int rr = wave + NW * i;
-          const int k = 8 * rr + (lane >> 3);
-          const uint32_t vo = min(k, nv - 1) * 1152 + 1024 + 16 * ((lane & 7) ^ swz(lane >> 3));
-          dma16(dst + LY::ROPE + rr * 1024, pbase, vo);
+        for (int t = 0; t < LY::DMA_PER_TILE / NW; ++t) {
+          const int i = wave + NW * t;
+          const int u = 64 * i + lane;
+          const int r = u / 72, x = u - 72 * r;
+          const uint32_t vo = min(r, nv - 1) * LY::PITCH + 16 * (x ^ LY::row_xor(r));
+          dma16(dst + 1024 * i, pbase, vo);
         }
       } else {
         const uint32_t rstride = (uint32_t)a.G * 256;  // bytes between tokens
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int ii = wave + NW * i;  // rows 4ii .. 4ii+3
           const int k = 4 * ii + (lane >> 4);
-          const uint32_t vo = min(k, nv - 1) * rstride + 16 * ((lane & 15) ^ swz(k & 7));
+          const uint32_t vo = min(k, nv - 1) * rstride + 16 * ((lane & 15) ^ LY::row_xor(k));
           dma16(dst + ii * 1024, kbase, vo);
           dma16(dst + LY::V_BASE + ii * 1024, vbase, vo);
         }
@@ -309,8 +312,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       // steps ahead
       auto k_addr = [&](int st) -> uint32_t {
         const int kb = st / KC, c = st % KC;
-        if (GQA || c < 16) return base + qk_off[c & 1] + kb * 16 * LY::K_PITCH + 128 * (c >> 1);
-        return base + rope_off[c & 1] + kb * 16 * LY::ROPE_PITCH;
+        if constexpr (GQA) return base + qk_off[c] + kb * 16 * LY::PITCH;
+        return base + qk_off[c & 1] + kb * 16 * LY::PITCH + 128 * (c >> 1);
       };
       constexpr int NQK = KB * KC;
       f32x4 s[KB];
@@ -384,10 +387,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
         auto v_frag = [&](int st) -> bf16x8 {
           const int cb = st / PC, c = st % PC;
-          const uint32_t a0 = base + v_off[cb & 3] + (32 * c) * LY::V_PITCH + 128 * (cb >> 2);
+          const uint32_t a0 = base + (32 * c) * LY::PITCH +
+                              (GQA ? v_off[cb % NVO] : v_off[cb & 3] + 128 * (cb >> 2));
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
           const bf16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * LY::V_PITCH));
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * LY::PITCH));
           return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         constexpr int NST = NCB * PC;
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         px[1] = pack_bf16x2(s[0][2], s[0][3]);
         const bf16x4 pf = __builtin_bit_cast(bf16x4, px);
         auto v_frag = [&](int cb) -> bf16x4 {
-          const uint32_t a0 = base + v_off[cb & 3] + 128 * (cb >> 2);
+          const uint32_t a0 = base + (GQA ? v_off[cb % NVO] : v_off[cb & 3] + 128 * (cb >> 2));
           return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
         };
         bf16x4 vf[3];

@@ -33,12 +33,6 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// LDS tiles hold token rows of 16-byte chunks. Chunk c of row k is stored at
-// chunk position k * chunks_per_row + (c ^ swz(k)). The XOR only touches the
-// low three bits of c, so it stays inside the row when chunks_per_row is a
-// multiple of 8, and it spreads eight consecutive rows (or four consecutive
-// rows read 32 bytes at a time) over distinct LDS banks.
-__device__ __forceinline__ int swz(int k) { return ((k & 3) << 1) | ((k >> 2) & 1); }
 
 __device__ __forceinline__ float wave_max32(float x) {
   // combine lane l with lane l ^ 32
