@@ -165,7 +165,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   static_assert(LY::DMA_PER_TILE % NW == 0 && NDMA < 64, "page copies split evenly");
 
   __shared__ __attribute__((aligned(1024))) char lds[2 * LY::TILE];
-  const uint32_t lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, lds);
+  lds_char* const lds_p = LDS_PTR(char, lds);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds_p;
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
@@ -306,25 +307,35 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         wait_vm<0>();
       }
       barrier();
-      const uint32_t base = lds0 + cur * LY::TILE;
+      // LDS operands are addressed as a per-lane pointer into this page's
+      // buffer plus a compile-time byte offset, which the compiler folds
+      // into the offset field of the LDS read.
+      lds_char* const buf = lds_p + cur * LY::TILE;
+      const lds_char* kp[NQO];
+#pragma unroll
+      for (int q = 0; q < NQO; ++q) kp[q] = buf + qk_off[q];
+      const lds_char* vp[NVO];
+#pragma unroll
+      for (int q = 0; q < NVO; ++q) vp[q] = buf + v_off[q];
 
       // S^T = K . Q^T, one 16-key block per kb; K fragments read two MFMA
       // steps ahead
-      auto k_addr = [&](int st) -> uint32_t {
+      auto k_frag = [&](int st) -> bf16x8 {
         const int kb = st / KC, c = st % KC;
-        if constexpr (GQA) return base + qk_off[c] + kb * 16 * LY::PITCH;
-        return base + qk_off[c & 1] + kb * 16 * LY::PITCH + 128 * (c >> 1);
+        const lds_char* p = GQA ? kp[c % NQO] + kb * 16 * LY::PITCH
+                                : kp[c & 1] + kb * 16 * LY::PITCH + 128 * (c >> 1);
+        return *(const __attribute__((address_space(3))) bf16x8*)p;
       };
       constexpr int NQK = KB * KC;
       f32x4 s[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
       bf16x8 kf[3];
-      kf[0] = *LDS_PTR(const bf16x8, k_addr(0));
-      kf[1] = *LDS_PTR(const bf16x8, k_addr(1));
+      kf[0] = k_frag(0);
+      kf[1] = k_frag(1);
 #pragma unroll
       for (int st = 0; st < NQK; ++st) {
-        if (st + 2 < NQK) kf[(st + 2) % 3] = *LDS_PTR(const bf16x8, k_addr(st + 2));
+        if (st + 2 < NQK) kf[(st + 2) % 3] = k_frag(st + 2);
         s[st / KC] = mfma16(kf[st % 3], qf[st % KC], s[st / KC]);
         mem_fence_compiler();
       }
@@ -387,11 +398,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
         auto v_frag = [&](int st) -> bf16x8 {
           const int cb = st / PC, c = st % PC;
-          const uint32_t a0 = base + (32 * c) * LY::PITCH +
-                              (GQA ? v_off[cb % NVO] : v_off[cb & 3] + 128 * (cb >> 2));
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
+          const lds_char* p = (32 * c) * LY::PITCH +
+                              (GQA ? vp[cb % NVO] : vp[cb & 3] + 128 * (cb >> 2));
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
           const bf16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0 + 16 * LY::PITCH));
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * LY::PITCH));
           return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         constexpr int NST = NCB * PC;
@@ -412,8 +423,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         px[1] = pack_bf16x2(s[0][2], s[0][3]);
         const bf16x4 pf = __builtin_bit_cast(bf16x4, px);
         auto v_frag = [&](int cb) -> bf16x4 {
-          const uint32_t a0 = base + (GQA ? v_off[cb % NVO] : v_off[cb & 3] + 128 * (cb >> 2));
-          return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(LDS_PTR(bf16x4, a0));
+          const lds_char* p = GQA ? vp[cb % NVO] : vp[cb & 3] + 128 * (cb >> 2);
+          return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
         };
         bf16x4 vf[3];
         vf[0] = v_frag(0);

@@ -1,5 +1,5 @@
 // Shared device definitions for the gfx950 decode kernels: vector types,
-// MFMA wrappers, the LDS tile swizzle and small helpers.
+// MFMA wrappers and small helpers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,6 +15,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
