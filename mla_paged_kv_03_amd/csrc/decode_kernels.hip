@@ -33,6 +33,8 @@
 //     K rows already in LDS, so every cache byte crosses HBM once.
 //   * Q (72 registers) stays in registers for the whole sequence; O^T (128
 //     fp32 registers for 512 columns) accumulates in registers.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "schedule.h"
@@ -106,6 +108,9 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t 
 
 // Softmax weights may exceed 1 by up to 2^RESCALE_SLACK before O is rescaled.
 constexpr float RESCALE_SLACK = 8.f;
+// With a fixed reference, weights up to 2^REF_LIMIT are accepted: sums of up
+// to 2^60 such terms times |V| stay far inside the fp32 range.
+constexpr float REF_LIMIT = 64.f;
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -292,10 +297,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
     const int vis = a.causal ? min(L - a.T + 1 + t, L) : L;
 
+    // One pass over the page range, accumulating O, l and the row reference
+    // m. FIXED: a row's m is the max of the first page on which the row sees
+    // a key (O and l are still exactly 0 then) and never moves afterwards;
+    // weights exp2(s - m) only grow, and fp32 holds them exactly in relative
+    // terms, so the pass is exact unless a later page exceeds m by more than
+    // REF_LIMIT, which it reports. Otherwise: the lazily rescaled online
+    // softmax, which cannot overflow. The fixed pass touches O with MFMA
+    // only, so O stays in the accumulator registers.
     f32x4 o[NCB];
+    float m, l;
+    auto run_range = [&](auto fixed_tag) -> bool {
+    constexpr bool FIXED = decltype(fixed_tag)::value;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
+    m = -INFINITY;
+    l = 0.f;
+    bool over = false;
 
     issue_page(p0, 0);
     for (int j = p0; j < p1; ++j) {
@@ -353,20 +371,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           tmax = fmaxf(tmax, x);
         }
       tmax = max4groups(tmax);
-      // Lazy rescale: m is a per-row reference, not the exact running max.
-      // Weights are exp2(s - m) <= 2^RESCALE_SLACK; only when a page raises
-      // a row's max by more than that (or gives the row its first key) are
-      // l and O rescaled to the new reference. l and O always share the
-      // same reference, so the final O / l and m + log2(l) are exact.
-      const bool need = tmax > m + RESCALE_SLACK;
-      if (__any(need)) {
-        // rows that do not need it keep alpha = 1 (a row that has seen no
-        // key yet has m = -inf, and exp2(m - m) would be NaN)
-        const float alpha = need ? fast_exp2(m - tmax) : 1.f;  // 0 when m = -inf
-        l *= alpha;
+      if constexpr (FIXED) {
+        if (m == -INFINITY) m = tmax;
+        over = over || tmax > m + REF_LIMIT;
+      } else {
+        // Lazy rescale: m is a per-row reference, not the exact running
+        // max. Weights are exp2(s - m) <= 2^RESCALE_SLACK; only when a page
+        // raises a row's max by more than that (or gives the row its first
+        // key) are l and O rescaled to the new reference. l and O always
+        // share the same reference, so O / l and m + log2(l) are exact.
+        const bool need = tmax > m + RESCALE_SLACK;
+        if (__any(need)) {
+          // rows that do not need it keep alpha = 1 (a row that has seen no
+          // key yet has m = -inf, and exp2(m - m) would be NaN)
+          const float alpha = need ? fast_exp2(m - tmax) : 1.f;  // 0 when m = -inf
+          l *= alpha;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
-        m = need ? tmax : m;
+          for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+          m = need ? tmax : m;
+        }
       }
       const float m_use = m == -INFINITY ? 0.f : m;
       float psum = 0.f;
@@ -438,6 +461,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       barrier();  // every wave is done with this buffer before it is refilled
     }
+    return over;
+    };
+    // every wave runs the same passes: the page buffers and barriers are shared
+    if (__syncthreads_or(run_range(std::true_type{}))) run_range(std::false_type{});
 
     // merge the key parts of each row group through LDS (page buffers are
     // free: every copy has landed and every wave has passed the last barrier)

@@ -250,21 +250,25 @@ def _climbing_scores(d, cfg, period=5, step=18.0, seed=7):
             d[kname][d["block_table"][b, j]] = f32_to_bf16_bits(alpha * q0 + noise)
 
 
+@pytest.mark.parametrize("period", [3, 5])
 @pytest.mark.parametrize("kind", ["mla", "gqa"])
-def test_scores_climbing_past_the_slack_rescale_the_running_sums(dev, kind):
-    """Scores that rise by more than the kernel's rescale slack from one page
-    to the next force the online-softmax rescale of O and l on page after
-    page; each worker here owns several consecutive pages (the batch has far
-    more pages than workers), so every worker rescales mid-range."""
+def test_scores_climbing_from_page_to_page(dev, kind, period):
+    """Scores rise by 18 (log2 units) from page to page within runs of
+    `period` pages, far more than the rescale slack. With period 3 a row's
+    scores end up to 36 above the first page's, which the fixed-reference
+    pass absorbs (weights up to 2^36); with period 5 the rise reaches 72,
+    past the fixed pass's limit, and ranges that start at the bottom of a
+    run fall back to the rescaling pass. Each worker owns several
+    consecutive pages (the batch has far more pages than workers)."""
     import mla_paged_kv_03_amd as lib
     Ls = (64 * 300, 64 * 280 + 17, 64 * 300, 64 * 290)
     cfg = (_mla(4, 1, 16, Ls, False) if kind == "mla" else _gqa(4, 1, 16, 2, Ls))
     d = inputs(cfg, seed=12)
-    _climbing_scores(d, cfg)
+    _climbing_scores(d, cfg, period=period)
     t = to_device(d, dev)
     plan = lib.mla_decode_plan(t["cache_seqlens"], cfg.s_q, cfg.h_q, cfg.h_kv, cfg.d_v)
     pages = int(((d["cache_seqlens"] + 63) // 64).sum())
     assert pages > 2 * plan.info.num_workers  # several pages per worker
     out, lse = run_gpu(d, t, plan=plan)
     ref_out, ref_lse = run_oracle(d)
-    check(out, lse, ref_out, ref_lse, f"climbing scores ({kind})")
+    check(out, lse, ref_out, ref_lse, f"climbing scores ({kind}, period {period})")
