@@ -106,6 +106,12 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t 
                : "memory", "m0");
 }
 
+// LDS operand reads are issued this many MFMA steps ahead of their use.
+#ifndef MLA_LDS_PREFETCH
+#define MLA_LDS_PREFETCH 6
+#endif
+constexpr int PF = MLA_LDS_PREFETCH;
+
 // Softmax weights may exceed 1 by up to 2^RESCALE_SLACK before O is rescaled.
 constexpr float RESCALE_SLACK = 8.f;
 // With a fixed reference, weights up to 2^REF_LIMIT are accepted: sums of up
@@ -336,26 +342,38 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int q = 0; q < NVO; ++q) vp[q] = buf + v_off[q];
 
-      // S^T = K . Q^T, one 16-key block per kb; K fragments read two MFMA
-      // steps ahead
+      // S^T = K . Q^T, one 16-key block per kb. Steps run d-chunk-major
+      // (st = c * KB + kb) into four accumulators (st % 4), so consecutive
+      // MFMAs never depend on each other; blocks that own several
+      // accumulators sum them afterwards. K fragments are read PF steps
+      // ahead of the MFMA that uses them.
       auto k_frag = [&](int st) -> bf16x8 {
-        const int kb = st / KC, c = st % KC;
+        const int c = st / KB, kb = st % KB;
         const lds_char* p = GQA ? kp[c % NQO] + kb * 16 * LY::PITCH
                                 : kp[c & 1] + kb * 16 * LY::PITCH + 128 * (c >> 1);
         return *(const __attribute__((address_space(3))) bf16x8*)p;
       };
       constexpr int NQK = KB * KC;
-      f32x4 s[KB];
+      constexpr int PFK = NQK < PF ? NQK : PF;
+      static_assert(KB <= 4 && 4 % KB == 0, "score blocks map onto four accumulators");
+      f32x4 acc[4];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      bf16x8 kf[3];
-      kf[0] = k_frag(0);
-      kf[1] = k_frag(1);
+      for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 kf[PFK + 1];
+#pragma unroll
+      for (int st = 0; st < PFK; ++st) kf[st] = k_frag(st);
 #pragma unroll
       for (int st = 0; st < NQK; ++st) {
-        if (st + 2 < NQK) kf[(st + 2) % 3] = k_frag(st + 2);
-        s[st / KC] = mfma16(kf[st % 3], qf[st % KC], s[st / KC]);
+        if (st + PFK < NQK) kf[(st + PFK) % (PFK + 1)] = k_frag(st + PFK);
+        acc[st % 4] = mfma16(kf[st % (PFK + 1)], qf[st / KB], acc[st % 4]);
         mem_fence_compiler();
+      }
+      f32x4 s[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] = acc[kb];
+#pragma unroll
+        for (int i = kb + KB; i < 4; i += KB) s[kb] += acc[i];
       }
 
       // scale, mask, running max over this wave's keys
@@ -419,8 +437,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           x[3] = pack_bf16x2(s[2 * c + 1][2], s[2 * c + 1][3]);
           pf[c] = __builtin_bit_cast(bf16x8, x);
         }
+        // steps run key-chunk-major (st = c * NCB + cb): consecutive MFMAs
+        // hit different output blocks; V^T fragments are read PF steps ahead
         auto v_frag = [&](int st) -> bf16x8 {
-          const int cb = st / PC, c = st % PC;
+          const int c = st / NCB, cb = st % NCB;
           const lds_char* p = (32 * c) * LY::PITCH +
                               (GQA ? vp[cb % NVO] : vp[cb & 3] + 128 * (cb >> 2));
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
@@ -429,13 +449,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         constexpr int NST = NCB * PC;
-        bf16x8 vf[3];
-        vf[0] = v_frag(0);
-        vf[1] = v_frag(1);
+        constexpr int PFV = NST < PF ? NST : PF;
+        bf16x8 vf[PFV + 1];
+#pragma unroll
+        for (int st = 0; st < PFV; ++st) vf[st] = v_frag(st);
 #pragma unroll
         for (int st = 0; st < NST; ++st) {
-          if (st + 2 < NST) vf[(st + 2) % 3] = v_frag(st + 2);
-          o[st / PC] = mfma16(vf[st % 3], pf[st % PC], o[st / PC]);
+          if (st + PFV < NST) vf[(st + PFV) % (PFV + 1)] = v_frag(st + PFV);
+          o[st % NCB] = mfma16(vf[st % (PFV + 1)], pf[st / NCB], o[st % NCB]);
           mem_fence_compiler();
         }
       } else {
@@ -449,13 +470,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           const lds_char* p = GQA ? vp[cb % NVO] : vp[cb & 3] + 128 * (cb >> 2);
           return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
         };
-        bf16x4 vf[3];
-        vf[0] = v_frag(0);
-        vf[1] = v_frag(1);
+        constexpr int PFV = NCB < PF ? NCB : PF;
+        bf16x4 vf[PFV + 1];
+#pragma unroll
+        for (int cb = 0; cb < PFV; ++cb) vf[cb] = v_frag(cb);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          if (cb + 2 < NCB) vf[(cb + 2) % 3] = v_frag(cb + 2);
-          o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[cb % 3], pf, o[cb], 0, 0, 0);
+          if (cb + PFV < NCB) vf[(cb + PFV) % (PFV + 1)] = v_frag(cb + PFV);
+          o[cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[cb % (PFV + 1)], pf, o[cb], 0, 0, 0);
           mem_fence_compiler();
         }
       }
