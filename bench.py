@@ -105,7 +105,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")

