@@ -1,6 +1,7 @@
 """Benchmark of the paged MLA decode hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py --op append [--config N] [--append-tokens T]
 
 One step is the whole path over one batch: the split-KV plan, the fused
 decode kernel and the split merge (mla_decode_plan + mla_decode, or
@@ -101,6 +102,73 @@ def cpu_baseline(d, budget_s=10.0):
                       f"fp64 numpy)"}
 
 
+def bench_append(args, cfg):
+    """The paged KV append alone: T new tokens per sequence written into the
+    config's cache (lengths count them), timed over back-to-back launches
+    with events on the stream. Bytes moved: every written row read once and
+    written once."""
+    import torch
+    import mla_paged_kv_03_amd as lib
+    from mla_paged_kv_03_amd import _lib
+    from workloads import make_inputs, f32_to_bf16_bits
+
+    dev = torch.device("cuda:0")
+    L = _lib.lib()
+    T = args.append_tokens or cfg.s_q
+    d = make_inputs(cfg)
+    B = cfg.batch
+    rng = np.random.default_rng(123)
+    bt = torch.from_numpy(d["block_table"]).to(dev)
+    sl = torch.from_numpy(d["cache_seqlens"]).to(dev)
+    P = ctypes.c_void_p
+    ptr = lambda x: P(x.data_ptr())
+    stream = P(torch.cuda.current_stream().cuda_stream)
+    tok = lambda shape: torch.from_numpy(
+        f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32)).view(np.int16)).to(dev)
+    if cfg.kind == "mla":
+        new = tok((B, T, cfg.d_qk))
+        cache = torch.from_numpy(d["kv"].view(np.int16)).to(dev)
+        row_bytes = cfg.d_qk * 2
+
+        def call():
+            return L.mla_kv_append(ptr(new), ptr(cache), ptr(bt), ptr(sl), B, T, d["num_pages"],
+                                   bt.shape[1], stream)
+    else:
+        nk, nv = tok((B, T, cfg.h_kv, cfg.d_qk)), tok((B, T, cfg.h_kv, cfg.d_v))
+        kc = torch.from_numpy(d["k"].view(np.int16)).to(dev)
+        vc = torch.from_numpy(d["v"].view(np.int16)).to(dev)
+        row_bytes = cfg.h_kv * (cfg.d_qk + cfg.d_v) * 2
+
+        def call():
+            return L.gqa_kv_append(ptr(nk), ptr(nv), ptr(kc), ptr(vc), ptr(bt), ptr(sl), B, T,
+                                   cfg.h_kv, d["num_pages"], bt.shape[1], stream)
+    written = int(np.minimum(d["cache_seqlens"].astype(np.int64), T).sum())
+    nbytes = 2 * written * row_bytes
+    for _ in range(args.warmup):
+        if call() != 0:
+            raise RuntimeError("append failed")
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        call()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / args.steps * 1e3
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "paged KV append GB/s (rows read + written)", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}_append_t{T}", "batch": B, "new_tokens": T,
+                   "rows_written": written, "row_bytes": row_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kv_append_kernel", "launch_avg_us": round(us, 2),
+                     "algorithmic_bytes_per_launch": nbytes}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +177,10 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--op", choices=["decode", "append"], default="decode",
+                    help="decode (the default step) or the paged KV append alone")
+    ap.add_argument("--append-tokens", type=int, default=0,
+                    help="new tokens per sequence for --op append (default: the config's s_q)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -134,6 +206,9 @@ def main():
     from workloads import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.config]
+    if args.op == "append":
+        bench_append(args, cfg)
+        return
     dev = torch.device("cuda:0")
     L = _lib.lib()
     sets = []

@@ -165,6 +165,36 @@ int attn_combine(const float* o_partial, const float* lse_partial, const int32_t
                  int32_t batch, int32_t rows_per_batch, int32_t dv, void* out, float* lse,
                  hipStream_t stream);
 
+/* Paged KV append: the step before decode that puts the s_q new tokens'
+ * cache rows into the paged cache (the KV cache kept in 64-token pages of
+ * the FlashMLA blog, "기술 기반"; KV Cache and PagedAttention among the
+ * related techniques of the Flash Attention wiki note, "지식 연결 (Graph)").
+ * cache_seqlens counts the new tokens, as in mla_decode: new token t of
+ * sequence b is position p = cache_seqlens[b] - s_q + t and goes to page
+ * block_table[b, p / 64], slot p % 64. A token with p < 0 (a sequence
+ * shorter than s_q) is not written; a block-table entry outside
+ * [0, num_pages) is skipped rather than written through. Only the new
+ * tokens' slots change; the copy is exact (bytes).
+ *
+ *   new_kv        bf16 [batch, s_q, 576] (in)
+ *   kv_cache      bf16 [num_pages, 64, 1, 576] (in/out)
+ *   block_table, cache_seqlens, num_pages, max_pages_per_seq: as for
+ *                 mla_decode (device, int32)
+ * Errors: MLA_ERR_BAD_SHAPE for negative sizes, s_q < 1 or unaligned
+ * tensors; MLA_ERR_NULL_ARG for a NULL pointer when batch > 0.
+ */
+int mla_kv_append(const void* new_kv, void* kv_cache, const int32_t* block_table,
+                  const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t num_pages,
+                  int32_t max_pages_per_seq, hipStream_t stream);
+
+/* The same for the GQA caches: new_k, new_v bf16 [batch, s_q, h_kv, 128]
+ * (in) go to k_cache, v_cache bf16 [num_pages, 64, h_kv, 128] (in/out),
+ * all h_kv groups of a token to the token's slot. 1 <= h_kv <= 4096. */
+int gqa_kv_append(const void* new_k, const void* new_v, void* k_cache, void* v_cache,
+                  const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                  int32_t s_q, int32_t h_kv, int32_t num_pages, int32_t max_pages_per_seq,
+                  hipStream_t stream);
+
 /* The plan's schedule computed on the host from host-resident lengths, for
  * checking the schedule on a machine without a GPU. num_workers, the
  * metadata layout and num_splits are exactly those mla_decode_plan would

@@ -20,7 +20,8 @@ from . import _lib
 from ._lib import DecodeError, PlanInfo
 
 __all__ = ["Plan", "PlanInfo", "DecodeError", "plan_info", "mla_decode_plan", "mla_decode",
-           "gqa_decode", "attn_combine", "mla_decode_plan_host", "profile_events"]
+           "gqa_decode", "attn_combine", "mla_kv_append", "gqa_kv_append",
+           "mla_decode_plan_host", "profile_events"]
 
 MLA_D, MLA_DV = 576, 512
 GQA_D = 128
@@ -152,6 +153,46 @@ def gqa_decode(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, c
         _ptr(plan.sched_metadata), _ptr(plan.num_splits), ws, wsb, _ptr(out), _ptr(lse),
         _stream()))
     return out, lse
+
+
+def mla_kv_append(new_kv, kv_cache, block_table, cache_seqlens):
+    """Write the s_q new tokens' latent rows into the paged cache in place.
+    new_kv bf16 [B, s_q, 576]; kv_cache bf16 [num_pages, 64, 1, 576];
+    cache_seqlens counts the new tokens (token t of sequence b is position
+    cache_seqlens[b] - s_q + t)."""
+    _need(new_kv, "new_kv", torch.bfloat16, 3)
+    _need(kv_cache, "kv_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, T, D = new_kv.shape
+    P, page, one, Dk = kv_cache.shape
+    if D != MLA_D or Dk != MLA_D or page != 64 or one != 1:
+        raise ValueError("mla_kv_append expects new_kv [B, s_q, 576], kv_cache [P, 64, 1, 576]")
+    _lib.check("mla_kv_append", _lib.lib().mla_kv_append(
+        _ptr(new_kv), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens), B, T, P,
+        block_table.shape[1], _stream()))
+    return kv_cache
+
+
+def gqa_kv_append(new_k, new_v, k_cache, v_cache, block_table, cache_seqlens):
+    """The same for the GQA caches: new_k, new_v bf16 [B, s_q, h_kv, 128];
+    k_cache, v_cache bf16 [num_pages, 64, h_kv, 128]."""
+    for t, n in ((new_k, "new_k"), (new_v, "new_v")):
+        _need(t, n, torch.bfloat16, 4)
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, T, G, D = new_k.shape
+    P, page, Gc, Dk = k_cache.shape
+    if (D != GQA_D or Dk != GQA_D or page != 64 or Gc != G or tuple(new_v.shape) != (B, T, G, D)
+            or tuple(v_cache.shape) != (P, 64, G, GQA_D)):
+        raise ValueError("gqa_kv_append expects new k/v [B, s_q, h_kv, 128] and "
+                         "k/v caches [P, 64, h_kv, 128]")
+    _lib.check("gqa_kv_append", _lib.lib().gqa_kv_append(
+        _ptr(new_k), _ptr(new_v), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(cache_seqlens), B, T, G, P, block_table.shape[1], _stream()))
+    return k_cache, v_cache
 
 
 def attn_combine(o_partial, lse_partial, num_splits, out=None, lse=None):

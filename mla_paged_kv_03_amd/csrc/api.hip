@@ -164,6 +164,33 @@ int run_decode(int B, int T, int H, int G, int DV, const void* q, const void* k,
   return MLA_OK;
 }
 
+// Shared checks and launch of the paged KV append (both cache shapes).
+int append_common(const void* src0, const void* src1, void* dst0, void* dst1,
+                  const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                  int32_t s_q, size_t row_bytes, int32_t num_pages, int32_t max_pages_per_seq,
+                  hipStream_t stream) {
+  if (batch < 0 || s_q < 1 || num_pages < 0 || max_pages_per_seq < 0) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)batch * s_q > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!src0 || !dst0 || !block_table || !cache_seqlens) return MLA_ERR_NULL_ARG;
+  if (src1 && !dst1) return MLA_ERR_NULL_ARG;
+  if (!aligned16(src0) || !aligned16(dst0) || (src1 && (!aligned16(src1) || !aligned16(dst1))))
+    return MLA_ERR_BAD_SHAPE;
+  mla::AppendArgs a;
+  a.src0 = (const char*)src0;
+  a.src1 = (const char*)src1;
+  a.dst0 = (char*)dst0;
+  a.dst1 = (char*)dst1;
+  a.block_table = block_table;
+  a.seqlens = cache_seqlens;
+  a.row_bytes = row_bytes;
+  a.B = batch;
+  a.T = s_q;
+  a.bt_stride = max_pages_per_seq;
+  a.num_pages = num_pages;
+  return mla::launch_kv_append(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,6 +252,23 @@ int attn_combine(const float* o_partial, const float* lse_partial, const int32_t
   c.lse = lse;
   c.B = batch; c.R = rows_per_batch; c.DV = dv;
   return mla::launch_combine_kernel(c, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_kv_append(const void* new_kv, void* kv_cache, const int32_t* block_table,
+                  const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t num_pages,
+                  int32_t max_pages_per_seq, hipStream_t stream) {
+  return append_common(new_kv, nullptr, kv_cache, nullptr, block_table, cache_seqlens, batch,
+                       s_q, (size_t)MLA_D * 2, num_pages, max_pages_per_seq, stream);
+}
+
+int gqa_kv_append(const void* new_k, const void* new_v, void* k_cache, void* v_cache,
+                  const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                  int32_t s_q, int32_t h_kv, int32_t num_pages, int32_t max_pages_per_seq,
+                  hipStream_t stream) {
+  if (h_kv < 1 || h_kv > 4096) return MLA_ERR_BAD_SHAPE;
+  if (batch > 0 && (!new_v || !v_cache)) return MLA_ERR_NULL_ARG;
+  return append_common(new_k, new_v, k_cache, v_cache, block_table, cache_seqlens, batch, s_q,
+                       (size_t)h_kv * GQA_D * 2, num_pages, max_pages_per_seq, stream);
 }
 
 int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q, int32_t h_q,

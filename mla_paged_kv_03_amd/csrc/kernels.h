@@ -35,6 +35,20 @@ struct CombineArgs {
   int B, R, DV;
 };
 
+struct AppendArgs {
+  const char* src0;            // [B, T] rows of row_bytes (MLA rows, or GQA K)
+  const char* src1;            // GQA V rows, or null
+  char* dst0;                  // cache [P, 64] rows of row_bytes
+  char* dst1;                  // GQA V cache, or null
+  const int32_t* block_table;  // [B, bt_stride]
+  const int32_t* seqlens;      // [B], counting the T new tokens
+  size_t row_bytes;            // a multiple of 16
+  int B, T, bt_stride, num_pages;
+};
+
+// Paged KV append: one wave per new token.
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t st);
+
 // One decode launch: grid = workers * row blocks, 64 * nw threads.
 hipError_t launch_decode_kernel(const DecodeArgs& a, int nw, bool gqa, int grid, hipStream_t st);
 // Split-KV merge of the partial results of split sequences.

@@ -19,7 +19,8 @@ def L():
 
 def test_every_declared_function_is_exported(L):
     names = _lib.header_functions()
-    assert {"mla_decode_plan", "mla_decode", "gqa_decode", "attn_combine"} <= set(names)
+    assert {"mla_decode_plan", "mla_decode", "gqa_decode", "attn_combine", "mla_kv_append",
+            "gqa_kv_append"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -80,6 +81,24 @@ def test_attn_combine_argument_checks(L):
     assert L.attn_combine(p, p, p, 2, 4, 12, p, p, None) == -2      # dv not a multiple of 8
     assert L.attn_combine(None, p, p, 2, 4, 16, p, p, None) == -1
     assert L.attn_combine(p, p, p, 0, 4, 16, p, p, None) == 0        # nothing to do
+
+
+def test_kv_append_argument_checks(L):
+    p = ctypes.c_void_p(64)
+    # new_kv, kv_cache, block_table, cache_seqlens, batch, s_q, num_pages, max_pages
+    assert L.mla_kv_append(p, p, p, p, 0, 1, 4, 4, None) == 0          # nothing to do
+    assert L.mla_kv_append(None, p, p, p, 2, 1, 4, 4, None) == -1
+    assert L.mla_kv_append(p, None, p, p, 2, 1, 4, 4, None) == -1
+    assert L.mla_kv_append(p, p, p, None, 2, 1, 4, 4, None) == -1
+    assert L.mla_kv_append(p, p, p, p, -1, 1, 4, 4, None) == -2
+    assert L.mla_kv_append(p, p, p, p, 2, 0, 4, 4, None) == -2
+    assert L.mla_kv_append(ctypes.c_void_p(72), p, p, p, 2, 1, 4, 4, None) == -2  # unaligned
+    assert L.mla_kv_append(p, p, p, p, 1 << 20, 1 << 12, 4, 4, None) == -3
+    # gqa: new_k, new_v, k_cache, v_cache, bt, sl, batch, s_q, h_kv, num_pages, max_pages
+    assert L.gqa_kv_append(p, None, p, p, p, p, 2, 1, 8, 4, 4, None) == -1
+    assert L.gqa_kv_append(p, p, p, None, p, p, 2, 1, 8, 4, 4, None) == -1
+    assert L.gqa_kv_append(p, p, p, p, p, p, 2, 1, 0, 4, 4, None) == -2
+    assert L.gqa_kv_append(p, p, p, p, p, p, 0, 1, 8, 4, 4, None) == 0
 
 
 # ------------------------------------------------------------ the schedule

@@ -10,16 +10,6 @@ from gpu_helpers import check, inputs, log, run_gpu, run_oracle, to_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def dev():
-    torch = pytest.importorskip("torch")
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import mla_paged_kv_03_amd as lib
-    lib._lib.lib()  # fail loudly if the library is missing
-    return torch.device("cuda:0")
-
-
 # ------------------------------------------------------------ small shapes
 def _mla(B, T, H, Ls, causal, **kw):
     return CONFIGS[3].with_(batch=B, s_q=T, h_q=H, causal=causal, seqlen_rule="fixed",
