@@ -9,20 +9,34 @@ namespace mla {
 constexpr int PLAN_THREADS = 1024;
 
 // Inclusive scan of one value per thread over the block; *total gets the
-// sum of all values.
-__device__ int block_scan(int v, int* buf, int* total) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < PLAN_THREADS; off <<= 1) {
-    const int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+// sum of all values. Each wave scans its 64 values with lane shuffles, wave
+// 0 scans the 16 wave totals: three barriers instead of two per doubling
+// step over the whole block.
+constexpr int PLAN_WAVES = PLAN_THREADS / 64;
+
+__device__ int block_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  const int r = buf[tid];
-  *total = buf[PLAN_THREADS - 1];
+  if (lane == 63) wsum[wv] = x;
   __syncthreads();
+  if (wv == 0) {
+    int t = lane < PLAN_WAVES ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < PLAN_WAVES; off <<= 1) {
+      const int y = __shfl_up(t, off);
+      if (lane >= off) t += y;
+    }
+    if (lane < PLAN_WAVES) wsum[lane] = t;
+  }
+  __syncthreads();
+  const int r = x + (wv > 0 ? wsum[wv - 1] : 0);
+  *total = wsum[PLAN_WAVES - 1];
+  __syncthreads();  // wsum is reused by the next scan
   return r;
 }
 
@@ -31,7 +45,7 @@ __device__ int block_scan(int v, int* buf, int* total) {
 // (B + 1 entries).
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqlens, int B, int W,
                                                            int32_t* meta, int32_t* slots) {
-  __shared__ int buf[PLAN_THREADS];
+  __shared__ int buf[PLAN_WAVES];
   const int tid = threadIdx.x;
   int32_t* prefix = meta + (size_t)W * sched::REC;
 

@@ -181,7 +181,11 @@ def test_device_plan_equals_host_plan(dev):
     import mla_paged_kv_03_amd as lib
     for Ls, T, H, G, dv in [((64, 200), 1, 8, 1, 512),
                             (tuple(np.random.default_rng(3).integers(0, 16385, 128)), 2, 128, 1, 512),
-                            ((8192,) * 256, 1, 16, 1, 512), ((100, 0, 70000), 1, 128, 8, 128)]:
+                            ((8192,) * 256, 1, 16, 1, 512), ((100, 0, 70000), 1, 128, 8, 128),
+                            # more sequences than the plan kernel's 1024 threads: the scans
+                            # carry across blocks of the batch
+                            (tuple(np.random.default_rng(5).integers(0, 3000, 2500)), 1, 16, 1, 512),
+                            (tuple([0] * 1500 + [1] * 700 + [64] * 30), 2, 128, 1, 512)]:
         sl = torch.tensor(Ls, dtype=torch.int32, device=dev)
         plan = lib.mla_decode_plan(sl, T, H, G, dv)
         torch.cuda.synchronize()
