@@ -71,6 +71,54 @@ CONFIGS = {
 }
 
 
+@dataclass(frozen=True)
+class GqlaConfig:
+    """A GQLA decode step: a latent cache plus per-group up-projections
+    (GQLA review, "2. Motivation & Problem Statement": the up-projections are
+    indexed by KV group, not by query head, so the same weights serve the
+    MQA-absorb path and the GQA path). Widths follow the DeepSeek-V3 shapes
+    of the latent row: d_c latent + d_r rope; each group's keys are d_h wide
+    plus the shared rope, its values d_v wide."""
+    name: str
+    seed: int
+    batch: int
+    s_q: int
+    h_q: int
+    h_kv: int            # KV groups; query head h uses group h // (h_q / h_kv)
+    causal: bool
+    seqlen_rule: str
+    seqlens_fixed: tuple = ()
+    seqlen_lo: int = 0
+    seqlen_hi: int = 0
+    q_std: float = 1.0
+    kv_std: float = 1.0
+    w_std: float = 1.0 / math.sqrt(512.0)
+    scale: float = 1.0 / math.sqrt(192.0)
+    d_c: int = 512
+    d_r: int = 64
+    d_h: int = 128
+    d_v: int = 128
+    page: int = PAGE
+
+    @property
+    def d_q(self) -> int:
+        """Width of a query row: d_h (no-rope part) + d_r (rope part)."""
+        return self.d_h + self.d_r
+
+    def with_(self, **kw) -> "GqlaConfig":
+        return replace(self, **kw)
+
+
+# With w_std = 1/sqrt(d_c) the expanded keys and values have unit variance,
+# so the scaled scores have about unit variance, as in the other workloads.
+GQLA_CONFIGS = {
+    "small": GqlaConfig("gqla_small_b3_h16_g4", 11, batch=3, s_q=2, h_q=16, h_kv=4,
+                        causal=True, seqlen_rule="fixed", seqlens_fixed=(1, 130, 300)),
+    "dsv3": GqlaConfig("gqla_dsv3_b64_h128_g8_L4096", 12, batch=64, s_q=1, h_q=128, h_kv=8,
+                       causal=False, seqlen_rule="fixed", seqlens_fixed=(4096,) * 64),
+}
+
+
 def bytes_per_token(cfg: DecodeConfig) -> int:
     """HBM bytes of one cached token for one sequence: the latent row for MLA,
     K and V rows of every KV head for GQA (bf16)."""

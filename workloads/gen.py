@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .configs import CONFIGS, DecodeConfig, PAGE
+from .configs import CONFIGS, DecodeConfig, GqlaConfig, PAGE
 
 BF16_NAN = np.uint16(0x7FC0)
 _CHUNK_PAGES = 256
@@ -121,3 +121,37 @@ def make_inputs(cfg: DecodeConfig, seed: int | None = None, seqlens=None,
 
 def config_inputs(idx: int, **kw) -> dict:
     return make_inputs(CONFIGS[idx], **kw)
+
+
+def make_gqla_inputs(cfg: GqlaConfig, seed: int | None = None, seqlens=None) -> dict:
+    """Draw one GQLA input set: the latent cache, queries and the per-group
+    up-projection weights (synthetic: there are no trained weights).
+
+    Draw order from ``default_rng(seed)``: cache_seqlens (unless fixed or
+    given), the page permutation, q [B, s_q, h_q, d_h + d_r], the latent cache
+    [P, 64, 1, d_c + d_r] (whole pages, tails included), then w_uk and w_uv
+    [h_kv, d_c, d_h | d_v]. All bf16 patterns (uint16), RNE from float32
+    normals times the config's std.
+    """
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    if seqlens is None:
+        L = draw_seqlens(cfg, rng)
+    else:
+        L = np.asarray(seqlens, dtype=np.int32)
+        assert L.shape == (cfg.batch,)
+    pages = (L.astype(np.int64) + PAGE - 1) // PAGE
+    num_pages = int(pages.sum())
+    max_pages = max(1, int(pages.max()) if len(pages) else 1)
+    perm = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((cfg.batch, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b in range(cfg.batch):
+        n = int(pages[b])
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    q = _normal_bf16(rng, (cfg.batch, cfg.s_q, cfg.h_q, cfg.d_q), cfg.q_std, chunk=1 << 30)
+    kv = _normal_bf16(rng, (num_pages, PAGE, 1, cfg.d_c + cfg.d_r), cfg.kv_std)
+    w_uk = _normal_bf16(rng, (cfg.h_kv, cfg.d_c, cfg.d_h), cfg.w_std, chunk=1 << 30)
+    w_uv = _normal_bf16(rng, (cfg.h_kv, cfg.d_c, cfg.d_v), cfg.w_std, chunk=1 << 30)
+    return dict(cfg=cfg, q=q, kv=kv, w_uk=w_uk, w_uv=w_uv, block_table=bt,
+                cache_seqlens=L, num_pages=num_pages)
