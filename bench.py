@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
     python bench.py --op append [--config N] [--append-tokens T]
+    python bench.py --op gqla
+
 
 One step is the whole path over one batch: the split-KV plan, the fused
 decode kernel and the split merge (mla_decode_plan + mla_decode, or
@@ -169,6 +171,181 @@ def bench_append(args, cfg):
                      "algorithmic_bytes_per_launch": nbytes}}), flush=True)
 
 
+def bench_gqla(args):
+    """GQLA's two decode paths from one set of synthetic weights, DeepSeek-V3
+    decode shape with 8 KV groups (64 sequences of 4096 tokens, 128 heads).
+
+    absorb step: absorbed queries (product with W_UK), plan, decode over the
+    latent cache, product with W_UV.  GQA step: plan, decode over the
+    expanded per-group caches. The expansion itself (once per cached token,
+    at append time) is timed on its own. Each part is timed over back-to-back
+    launches with events on the stream; the decode kernels alone with the
+    library's profiling events."""
+    import torch
+    import mla_paged_kv_03_amd as lib
+    from mla_paged_kv_03_amd import _lib
+    from workloads import GQLA_CONFIGS, make_gqla_inputs
+
+    cfg = GQLA_CONFIGS["dsv3"]
+    dev = torch.device("cuda:0")
+    L = _lib.lib()
+    d = make_gqla_inputs(cfg)
+    B, T, H, G = cfg.batch, cfg.s_q, cfg.h_q, cfg.h_kv
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    q, kv, wk, wv = bf(d["q"]), bf(d["kv"]), bf(d["w_uk"]), bf(d["w_uv"])
+    bt = torch.from_numpy(d["block_table"]).to(dev)
+    sl = torch.from_numpy(d["cache_seqlens"]).to(dev)
+    P = lambda x: ctypes.c_void_p(x.data_ptr()) if x is not None else None
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    NP, maxp = kv.shape[0], bt.shape[1]
+    rows = NP * 64
+    k_rows = torch.empty(NP, 64, G, 192, dtype=torch.bfloat16, device=dev)
+    v_rows = torch.empty(NP, 64, G, 128, dtype=torch.bfloat16, device=dev)
+    qa = torch.empty(B, T, H, 576, dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty(B, T, H, 512, dtype=torch.bfloat16, device=dev)
+    out_a = torch.empty(B, T, H, 128, dtype=torch.bfloat16, device=dev)
+    out_g = torch.empty(B, T, H, 128, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=dev)
+    plan_a = lib.mla_decode_plan(sl, T, H, 1, 512)
+    plan_g = lib.mla_decode_plan(sl, T, H, G, 128)
+    ia, ig = plan_a.info, plan_g.info
+    wsa, wsba = lib._ws(plan_a)
+    wsg, wsbg = lib._ws(plan_g)
+    scale = cfg.scale
+
+    def ok(name, rc):
+        if rc != 0:
+            raise RuntimeError(f"{name} failed with {rc}")
+
+    def expand():
+        ok("gqla_expand_kv", L.gqla_expand_kv(P(kv), P(wk), P(wv), P(k_rows), P(v_rows), rows, G,
+                                              stream))
+
+    def absorb_q():
+        ok("gqla_absorb_query", L.gqla_absorb_query(P(q), P(wk), P(qa), B * T, H, G, stream))
+
+    def absorb_o():
+        ok("gqla_absorb_output", L.gqla_absorb_output(P(o_lat), P(wv), P(out_a), B * T, H, G,
+                                                      stream))
+
+    def decode_a():
+        ok("mla_decode_plan", L.mla_decode_plan(P(sl), B, T, H, 1, 512, P(plan_a.sched_metadata),
+                                                P(plan_a.num_splits), ctypes.byref(ia), stream))
+        ok("mla_decode", L.mla_decode(P(qa), P(kv), P(bt), P(sl), B, T, H, NP, maxp, scale, 0,
+                                      P(plan_a.sched_metadata), P(plan_a.num_splits), wsa, wsba,
+                                      P(o_lat), P(lse), stream))
+
+    def decode_g():
+        ok("mla_decode_plan", L.mla_decode_plan(P(sl), B, T, H, G, 128, P(plan_g.sched_metadata),
+                                                P(plan_g.num_splits), ctypes.byref(ig), stream))
+        ok("gqla_decode", L.gqla_decode(P(q), P(k_rows), P(v_rows), P(bt), P(sl), B, T, H, G, NP,
+                                        maxp, scale, 0, P(plan_g.sched_metadata),
+                                        P(plan_g.num_splits), wsg, wsbg, P(out_g), P(lse),
+                                        stream))
+
+    def absorb_step():
+        absorb_q()
+        decode_a()
+        absorb_o()
+
+    hip = ctypes.CDLL("libamdhip64.so")
+
+    def timed(fn, n, events=False):
+        """Average us per call over n back-to-back calls; with events, also
+        the decode kernel alone (raw HIP events handed to the library's
+        hook, which records them on the kernel's stream)."""
+        for _ in range(max(1, n // 4)):
+            fn()
+        torch.cuda.synchronize()
+        ev = []
+        if events:
+            for _ in range(2 * n):
+                h = ctypes.c_void_p()
+                if hip.hipEventCreate(ctypes.byref(h)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                ev.append(h)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(n):
+            if events:
+                L.mla_profile_events(ev[2 * i], ev[2 * i + 1])
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        L.mla_profile_events(None, None)
+        us = t0.elapsed_time(t1) / n * 1e3
+        kus = None
+        if events:
+            tot = 0.0
+            for i in range(n):
+                ms = ctypes.c_float()
+                if hip.hipEventElapsedTime(ctypes.byref(ms), ev[2 * i], ev[2 * i + 1]) != 0:
+                    raise RuntimeError("hipEventElapsedTime failed")
+                tot += ms.value
+            for h in ev:
+                hip.hipEventDestroy(h)
+            kus = tot / n * 1e3
+        return us, kus
+
+    expand()
+    torch.cuda.synchronize()
+    n = args.steps
+    t_exp, _ = timed(expand, max(5, n // 20))
+    t_aq, _ = timed(absorb_q, n)
+    t_ao, _ = timed(absorb_o, n)
+    t_a, k_a = timed(absorb_step, n, events=True)
+    t_g, k_g = timed(decode_g, n, events=True)
+    tokens = B * T
+    toks = lambda us: tokens / (us * 1e-6)
+    ctx = int(d["cache_seqlens"].astype(np.int64).sum())
+    lat_bytes = ctx * 576 * 2 + B * T * H * (576 + 512) * 2 + B * T * H * 4
+    gqa_bytes = ctx * G * (192 + 128) * 2 + B * T * H * (192 + 128) * 2 + B * T * H * 4
+    lat_flops = 2 * T * H * ctx * (576 + 512)
+    gqa_flops = 2 * T * H * ctx * (192 + 128)
+    proj_flops = 2 * B * T * H * 128 * 512
+    exp_flops = 2 * rows * 512 * (128 + 128) * G
+    exp_bytes = rows * 576 * 2 + rows * G * (192 + 128) * 2 + 2 * G * 512 * 128 * 2
+
+    def roof(nbytes, flops, us):
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+        t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
+        if t_hbm >= t_mfma:
+            ach = nbytes / (us * 1e-6) / 1e9
+            return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4)}
+        ach = flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+    print(f"[bench] gqla: absorb step {t_a:.1f} us (decode kernel {k_a:.1f}, absorb q "
+          f"{t_aq:.1f}, absorb out {t_ao:.1f}); GQA step {t_g:.1f} us (decode kernel "
+          f"{k_g:.1f}); expansion of {rows} rows {t_exp:.1f} us", flush=True)
+    best = min(t_a, t_g)
+    print(json.dumps({
+        "metric": "GQLA decode tokens/s, faster of the MQA-absorb and GQA paths (same weights)",
+        "value": round(toks(best), 1), "unit": "tokens/s", "n_gpus": 1, "steps": n,
+        "warmup": max(1, n // 4), "ms_per_step": round(best / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (random latent cache and random group up-projections)",
+        "config": {"workload": cfg.name, "batch": B, "s_q": T, "h_q": H, "h_kv": G,
+                   "seqlen_total": ctx},
+        "paths": {
+            "absorb": {"us_per_step": round(t_a, 2), "tokens_per_s": round(toks(t_a), 1),
+                       "decode_kernel_us": round(k_a, 2), "absorb_query_us": round(t_aq, 2),
+                       "absorb_output_us": round(t_ao, 2),
+                       "decode_roofline": roof(lat_bytes, lat_flops, k_a),
+                       "projection_flops_each": proj_flops},
+            "gqa": {"us_per_step": round(t_g, 2), "tokens_per_s": round(toks(t_g), 1),
+                    "decode_kernel_us": round(k_g, 2),
+                    "decode_roofline": roof(gqa_bytes, gqa_flops, k_g)},
+            "faster": "absorb" if t_a <= t_g else "gqa"},
+        "expansion": {"rows": rows, "us": round(t_exp, 1),
+                      "roofline": roof(exp_bytes, exp_flops, t_exp),
+                      "tflops": round(exp_flops / (t_exp * 1e-6) / 1e12, 1),
+                      "algorithmic_bytes": exp_bytes, "flops": exp_flops}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,8 +354,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--op", choices=["decode", "append"], default="decode",
-                    help="decode (the default step) or the paged KV append alone")
+    ap.add_argument("--op", choices=["decode", "append", "gqla"], default="decode",
+                    help="decode (the default step), the paged KV append alone, or GQLA's "
+                         "two decode paths")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="new tokens per sequence for --op append (default: the config's s_q)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -206,6 +384,9 @@ def main():
     from workloads import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.config]
+    if args.op == "gqla":
+        bench_gqla(args)
+        return
     if args.op == "append":
         bench_append(args, cfg)
         return

@@ -195,6 +195,79 @@ int gqa_kv_append(const void* new_k, const void* new_v, void* k_cache, void* v_c
                   int32_t s_q, int32_t h_kv, int32_t num_pages, int32_t max_pages_per_seq,
                   hipStream_t stream);
 
+/* ---- GQLA: one set of group-indexed weights, two decode paths ----
+ *
+ * GQLA (GQLA review, "2. Motivation & Problem Statement" and Figure 2) keeps
+ * MLA's latent cache row [c (512), k_rope (64)] but indexes the key and value
+ * up-projections by KV group: W_UK^g and W_UV^g, bf16 [h_kv, 512, 128], with
+ * query head h in group g = h / (h_q / h_kv). Group g's key for a token is
+ * [c W_UK^g, k_rope] (192 wide) and its value c W_UV^g (128 wide); a query
+ * row is [q_nope (128), q_rope (64)]. The same weights give two decode paths
+ * ("1. Key Terms & Definitions"):
+ *   - MQA-absorb: gqla_absorb_query, then mla_decode over the latent cache
+ *     (scale 1/sqrt(192)), then gqla_absorb_output;
+ *   - GQA: gqla_expand_kv once per cached token (at append time), then
+ *     gqla_decode over the expanded per-group caches.
+ * The two agree up to rounding. The products run on bf16 MFMA with fp32
+ * accumulation; every product output is rounded to bf16 (nearest-even).
+ * Weights are [group][latent column][output column], row-major.
+ */
+
+/* Expanded per-group K and V rows of cached tokens (GQA path).
+ *
+ *   kv_rows  bf16 [n_rows, 576] (in): latent rows, e.g. a whole cache
+ *            [num_pages, 64, 1, 576] (n_rows = 64 * num_pages) or the new
+ *            tokens of an append [batch, s_q, 576]
+ *   w_uk     bf16 [h_kv, 512, 128] (in); w_uv bf16 [h_kv, 512, 128] (in)
+ *   k_rows   bf16 [n_rows, h_kv, 192] (out): [c W_UK^g, k_rope]
+ *   v_rows   bf16 [n_rows, h_kv, 128] (out): c W_UV^g
+ * A cache expanded page for page keeps the page layout of gqla_decode's
+ * caches. Errors: MLA_ERR_BAD_SHAPE for n_rows < 0, h_kv outside 1..4096 or
+ * unaligned tensors; MLA_ERR_UNSUPPORTED for n_rows > 2^31 - 1;
+ * MLA_ERR_NULL_ARG for a NULL pointer when n_rows > 0. */
+int gqla_expand_kv(const void* kv_rows, const void* w_uk, const void* w_uv, void* k_rows,
+                   void* v_rows, int64_t n_rows, int32_t h_kv, hipStream_t stream);
+
+/* Absorbed queries (MQA-absorb path): q_absorbed[n, h] =
+ * [q_nope[n, h] W_UK^g^T, q_rope[n, h]], so that q_absorbed . latent row =
+ * q . (group g's key).
+ *
+ *   q           bf16 [n_tokens, h_q, 192] (in), e.g. [batch, s_q, h_q, 192]
+ *   w_uk        bf16 [h_kv, 512, 128] (in)
+ *   q_absorbed  bf16 [n_tokens, h_q, 576] (out): mla_decode's q
+ * Errors: MLA_ERR_BAD_SHAPE for n_tokens < 0, h_q < 1, h_kv < 1,
+ * h_q % h_kv != 0 or unaligned tensors; MLA_ERR_UNSUPPORTED for h_kv > 65535
+ * or n_tokens * h_q / h_kv near 2^31; MLA_ERR_NULL_ARG for a NULL pointer
+ * when n_tokens > 0. */
+int gqla_absorb_query(const void* q, const void* w_uk, void* q_absorbed, int32_t n_tokens,
+                      int32_t h_q, int32_t h_kv, hipStream_t stream);
+
+/* Output of the MQA-absorb path: out[n, h] = o_latent[n, h] W_UV^g.
+ *
+ *   o_latent  bf16 [n_tokens, h_q, 512] (in): mla_decode's out
+ *   w_uv      bf16 [h_kv, 512, 128] (in)
+ *   out       bf16 [n_tokens, h_q, 128] (out)
+ * Errors as for gqla_absorb_query. */
+int gqla_absorb_output(const void* o_latent, const void* w_uv, void* out, int32_t n_tokens,
+                       int32_t h_q, int32_t h_kv, hipStream_t stream);
+
+/* Decode on the GQA path over expanded caches (gqla_expand_kv's layout).
+ *
+ *   q        bf16 [batch, s_q, h_q, 192]
+ *   k_cache  bf16 [num_pages, 64, h_kv, 192]
+ *   v_cache  bf16 [num_pages, 64, h_kv, 128]
+ *   out      bf16 [batch, s_q, h_q, 128] (out); lse fp32 [batch, s_q, h_q]
+ *   softmax_scale multiplies the full 192-wide q.k (1/sqrt(192))
+ * The plan comes from mla_decode_plan with the same h_kv and
+ * head_dim_v = 128 (as for gqa_decode). Other arguments, preconditions and
+ * errors as for gqa_decode. */
+int gqla_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                int32_t s_q, int32_t h_q, int32_t h_kv, int32_t num_pages,
+                int32_t max_pages_per_seq, float softmax_scale, int32_t causal,
+                const int32_t* sched_metadata, const int32_t* num_splits, void* workspace,
+                size_t workspace_bytes, void* out, float* lse, hipStream_t stream);
+
 /* The plan's schedule computed on the host from host-resident lengths, for
  * checking the schedule on a machine without a GPU. num_workers, the
  * metadata layout and num_splits are exactly those mla_decode_plan would

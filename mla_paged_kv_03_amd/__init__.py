@@ -21,10 +21,13 @@ from ._lib import DecodeError, PlanInfo
 
 __all__ = ["Plan", "PlanInfo", "DecodeError", "plan_info", "mla_decode_plan", "mla_decode",
            "gqa_decode", "attn_combine", "mla_kv_append", "gqa_kv_append",
+           "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output", "gqla_decode",
            "mla_decode_plan_host", "profile_events"]
 
 MLA_D, MLA_DV = 576, 512
 GQA_D = 128
+GQLA_DC, GQLA_DR, GQLA_DH, GQLA_DV = 512, 64, 128, 128
+GQLA_DQ = GQLA_DH + GQLA_DR
 
 
 def _ptr(t):
@@ -193,6 +196,116 @@ def gqa_kv_append(new_k, new_v, k_cache, v_cache, block_table, cache_seqlens):
         _ptr(new_k), _ptr(new_v), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(cache_seqlens), B, T, G, P, block_table.shape[1], _stream()))
     return k_cache, v_cache
+
+
+def _gqla_weights(w_uk, w_uv=None):
+    _need(w_uk, "w_uk", torch.bfloat16, 3)
+    G = w_uk.shape[0]
+    if tuple(w_uk.shape) != (G, GQLA_DC, GQLA_DH):
+        raise ValueError("w_uk must be [h_kv, 512, 128]")
+    if w_uv is not None:
+        _need(w_uv, "w_uv", torch.bfloat16, 3)
+        if tuple(w_uv.shape) != (G, GQLA_DC, GQLA_DV):
+            raise ValueError("w_uv must be [h_kv, 512, 128] with the same h_kv as w_uk")
+    return G
+
+
+def gqla_expand_kv(kv_rows, w_uk, w_uv, k_rows=None, v_rows=None):
+    """GQLA's GQA-path cache: per group g, K = [c W_UK^g, k_rope] and
+    V = c W_UV^g of every latent row. kv_rows bf16 [..., 576] (e.g. a cache
+    [P, 64, 1, 576]); returns k_rows [..., h_kv, 192] and v_rows
+    [..., h_kv, 128] (the leading dims of kv_rows, a trailing 1 dropped)."""
+    _need(kv_rows, "kv_rows", torch.bfloat16)
+    G = _gqla_weights(w_uk, w_uv)
+    if kv_rows.shape[-1] != GQLA_DC + GQLA_DR:
+        raise ValueError("kv_rows must end in 576 columns")
+    lead = tuple(kv_rows.shape[:-1])
+    if len(lead) >= 2 and lead[-1] == 1:
+        lead = lead[:-1]
+    n = kv_rows.numel() // (GQLA_DC + GQLA_DR)
+    if k_rows is None:
+        k_rows = torch.empty(lead + (G, GQLA_DQ), dtype=torch.bfloat16, device=kv_rows.device)
+    if v_rows is None:
+        v_rows = torch.empty(lead + (G, GQLA_DV), dtype=torch.bfloat16, device=kv_rows.device)
+    _need(k_rows, "k_rows", torch.bfloat16)
+    _need(v_rows, "v_rows", torch.bfloat16)
+    if k_rows.numel() != n * G * GQLA_DQ or v_rows.numel() != n * G * GQLA_DV:
+        raise ValueError("k_rows / v_rows do not match kv_rows and h_kv")
+    _lib.check("gqla_expand_kv", _lib.lib().gqla_expand_kv(
+        _ptr(kv_rows), _ptr(w_uk), _ptr(w_uv), _ptr(k_rows), _ptr(v_rows), n, G, _stream()))
+    return k_rows, v_rows
+
+
+def gqla_absorb_query(q, w_uk, out=None):
+    """The MQA-absorb path's queries: [q_nope W_UK^g^T, q_rope] per head.
+    q bf16 [B, s_q, h_q, 192] -> bf16 [B, s_q, h_q, 576] (mla_decode's q)."""
+    _need(q, "q", torch.bfloat16, 4)
+    G = _gqla_weights(w_uk)
+    B, T, H, D = q.shape
+    if D != GQLA_DQ:
+        raise ValueError("q must be [B, s_q, h_q, 192]")
+    if out is None:
+        out = torch.empty(B, T, H, GQLA_DC + GQLA_DR, dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, 4)
+    if tuple(out.shape) != (B, T, H, GQLA_DC + GQLA_DR):
+        raise ValueError("out must be [B, s_q, h_q, 576]")
+    _lib.check("gqla_absorb_query", _lib.lib().gqla_absorb_query(
+        _ptr(q), _ptr(w_uk), _ptr(out), B * T, H, G, _stream()))
+    return out
+
+
+def gqla_absorb_output(o_latent, w_uv, out=None):
+    """The MQA-absorb path's output: o_latent W_UV^g per head.
+    o_latent bf16 [B, s_q, h_q, 512] -> bf16 [B, s_q, h_q, 128]."""
+    _need(o_latent, "o_latent", torch.bfloat16, 4)
+    _need(w_uv, "w_uv", torch.bfloat16, 3)
+    G = w_uv.shape[0]
+    if tuple(w_uv.shape) != (G, GQLA_DC, GQLA_DV):
+        raise ValueError("w_uv must be [h_kv, 512, 128]")
+    B, T, H, D = o_latent.shape
+    if D != GQLA_DC:
+        raise ValueError("o_latent must be [B, s_q, h_q, 512]")
+    if out is None:
+        out = torch.empty(B, T, H, GQLA_DV, dtype=torch.bfloat16, device=o_latent.device)
+    _need(out, "out", torch.bfloat16, 4)
+    if tuple(out.shape) != (B, T, H, GQLA_DV):
+        raise ValueError("out must be [B, s_q, h_q, 128]")
+    _lib.check("gqla_absorb_output", _lib.lib().gqla_absorb_output(
+        _ptr(o_latent), _ptr(w_uv), _ptr(out), B * T, H, G, _stream()))
+    return out
+
+
+def gqla_decode(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, causal=False,
+                plan: Plan | None = None, out=None, lse=None):
+    """GQLA's GQA path: q bf16 [B, s_q, h_q, 192] over the expanded caches
+    k_cache bf16 [P, 64, h_kv, 192], v_cache bf16 [P, 64, h_kv, 128]. The
+    plan is the GQA one (h_kv, head_dim_v = 128)."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, T, H, D = q.shape
+    P, page, G, Dk = k_cache.shape
+    if (D != GQLA_DQ or Dk != GQLA_DQ or page != 64
+            or tuple(v_cache.shape) != (P, 64, G, GQLA_DV)):
+        raise ValueError("gqla_decode expects q [..., 192], k_cache [P, 64, h_kv, 192] and "
+                         "v_cache [P, 64, h_kv, 128]")
+    if plan is None:
+        plan = mla_decode_plan(cache_seqlens, T, H, G, GQLA_DV)
+    if plan.shape != (B, T, H, G, GQLA_DV):
+        raise ValueError(f"plan was made for {plan.shape}")
+    if out is None:
+        out = torch.empty(B, T, H, GQLA_DV, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    ws, wsb = _ws(plan)
+    _lib.check("gqla_decode", _lib.lib().gqla_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(cache_seqlens), B, T, H,
+        G, P, block_table.shape[1], float(softmax_scale), int(bool(causal)),
+        _ptr(plan.sched_metadata), _ptr(plan.num_splits), ws, wsb, _ptr(out), _ptr(lse),
+        _stream()))
+    return out, lse
 
 
 def attn_combine(o_partial, lse_partial, num_splits, out=None, lse=None):

@@ -32,6 +32,11 @@ _SIGS = {
     "attn_combine": [_P, _P, _P, _I, _I, _I, _P, _P, _P],
     "mla_kv_append": [_P, _P, _P, _P, _I, _I, _I, _I, _P],
     "gqa_kv_append": [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P],
+    "gqla_decode": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
+                    ctypes.c_size_t, _P, _P, _P],
+    "gqla_absorb_query": [_P, _P, _P, _I, _I, _I, _P],
+    "gqla_absorb_output": [_P, _P, _P, _I, _I, _I, _P],
+    "gqla_expand_kv": [_P, _P, _P, _P, _P, ctypes.c_int64, _I, _P],
     "mla_decode_plan_host": [_P, _I, _I, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PlanInfo)],
     "mla_status_string": [ctypes.c_int],
     "mla_profile_events": [_P, _P],

@@ -13,6 +13,9 @@ namespace {
 
 constexpr int MLA_D = 576, MLA_DV = 512;  // latent row: 512 latent + 64 rope
 constexpr int GQA_D = 128, GQA_DV = 128;
+// GQLA widths: latent d_c, rope d_r, per-group key (no-rope) d_h and value d_v
+constexpr int GQLA_DC = 512, GQLA_DR = 64, GQLA_DH = 128, GQLA_DVG = 128;
+constexpr int GQLA_DQ = GQLA_DH + GQLA_DR;  // query and expanded key width (192)
 constexpr int MAX_DEVICES = 64;
 int g_cu_count[MAX_DEVICES];  // 0 = not queried yet
 hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;  // mla_profile_events
@@ -112,7 +115,8 @@ int check_decode_args(bool gqa, const void* q, const void* k, const void* v,
   return MLA_OK;
 }
 
-int run_decode(int B, int T, int H, int G, int DV, const void* q, const void* k, const void* v,
+int run_decode(int B, int T, int H, int G, int DV, bool rope_k, const void* q, const void* k,
+               const void* v,
                const int32_t* block_table, const int32_t* seqlens, int num_pages,
                int max_pages, float scale, int causal, const int32_t* meta,
                const int32_t* splits, void* ws, size_t ws_bytes, void* out, float* lse,
@@ -149,7 +153,8 @@ int run_decode(int B, int T, int H, int G, int DV, const void* q, const void* k,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.causal = causal;
   if (g_prof_start && hipEventRecord(g_prof_start, st) != hipSuccess) return MLA_ERR_HIP;
-  if (mla::launch_decode_kernel(a, g.nw, g.gqa, g.W * g.RB, st) != hipSuccess) return MLA_ERR_HIP;
+  const int kind = !g.gqa ? mla::KIND_MLA : rope_k ? mla::KIND_GQA_ROPE : mla::KIND_GQA;
+  if (mla::launch_decode_kernel(a, g.nw, kind, g.W * g.RB, st) != hipSuccess) return MLA_ERR_HIP;
   if (g_prof_stop && hipEventRecord(g_prof_stop, st) != hipSuccess) return MLA_ERR_HIP;
   if (g.max_slots > 0) {
     mla::CombineArgs c;
@@ -191,6 +196,14 @@ int append_common(const void* src0, const void* src1, void* dst0, void* dst1,
   return mla::launch_kv_append(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+// Head counts of the GQLA projections.
+int gqla_heads(int32_t n_tokens, int32_t h_q, int32_t h_kv) {
+  if (n_tokens < 0 || h_q < 1 || h_kv < 1 || h_q % h_kv != 0) return MLA_ERR_BAD_SHAPE;
+  if (h_kv > 65535 || (int64_t)n_tokens * (h_q / h_kv) > 0x7fffffffLL - 128)
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,7 +234,7 @@ int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
                int32_t causal, const int32_t* sched_metadata, const int32_t* num_splits,
                void* workspace, size_t workspace_bytes, void* out, float* lse,
                hipStream_t stream) {
-  return run_decode(batch, s_q, h_q, 1, MLA_DV, q, kv_cache, nullptr, block_table, cache_seqlens, num_pages,
+  return run_decode(batch, s_q, h_q, 1, MLA_DV, false, q, kv_cache, nullptr, block_table, cache_seqlens, num_pages,
                     max_pages_per_seq, softmax_scale, causal, sched_metadata, num_splits,
                     workspace, workspace_bytes, out, lse, stream);
 }
@@ -232,7 +245,7 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                int32_t max_pages_per_seq, float softmax_scale, int32_t causal,
                const int32_t* sched_metadata, const int32_t* num_splits, void* workspace,
                size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
-  return run_decode(batch, s_q, h_q, h_kv, GQA_DV, q, k_cache, v_cache, block_table, cache_seqlens, num_pages,
+  return run_decode(batch, s_q, h_q, h_kv, GQA_DV, false, q, k_cache, v_cache, block_table, cache_seqlens, num_pages,
                     max_pages_per_seq, softmax_scale, causal, sched_metadata, num_splits,
                     workspace, workspace_bytes, out, lse, stream);
 }
@@ -269,6 +282,99 @@ int gqa_kv_append(const void* new_k, const void* new_v, void* k_cache, void* v_c
   if (batch > 0 && (!new_v || !v_cache)) return MLA_ERR_NULL_ARG;
   return append_common(new_k, new_v, k_cache, v_cache, block_table, cache_seqlens, batch, s_q,
                        (size_t)h_kv * GQA_D * 2, num_pages, max_pages_per_seq, stream);
+}
+
+int gqla_decode(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                int32_t s_q, int32_t h_q, int32_t h_kv, int32_t num_pages,
+                int32_t max_pages_per_seq, float softmax_scale, int32_t causal,
+                const int32_t* sched_metadata, const int32_t* num_splits, void* workspace,
+                size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
+  return run_decode(batch, s_q, h_q, h_kv, GQLA_DVG, true, q, k_cache, v_cache, block_table,
+                    cache_seqlens, num_pages, max_pages_per_seq, softmax_scale, causal,
+                    sched_metadata, num_splits, workspace, workspace_bytes, out, lse, stream);
+}
+
+int gqla_absorb_query(const void* q, const void* w_uk, void* q_absorbed, int32_t n_tokens,
+                      int32_t h_q, int32_t h_kv, hipStream_t stream) {
+  int rc;
+  if ((rc = gqla_heads(n_tokens, h_q, h_kv)) != MLA_OK) return rc;
+  if (n_tokens == 0) return MLA_OK;
+  if (!q || !w_uk || !q_absorbed) return MLA_ERR_NULL_ARG;
+  if (!aligned16(q) || !aligned16(w_uk) || !aligned16(q_absorbed)) return MLA_ERR_BAD_SHAPE;
+  const int hpg = h_q / h_kv;
+  mla::GemmArgs a = {};
+  a.a = (const uint16_t*)q;
+  a.inner = hpg;
+  a.a_outer = (int64_t)h_q * GQLA_DQ; a.a_inner = GQLA_DQ; a.a_batch = (int64_t)hpg * GQLA_DQ;
+  a.b = (const uint16_t*)w_uk;  // [c][i]: row c of W_UK^g is column c of the product
+  a.b_batch = (int64_t)GQLA_DC * GQLA_DH; a.ldb = GQLA_DH; a.b_kn = 0;
+  a.c = (uint16_t*)q_absorbed;
+  a.c_outer = (int64_t)h_q * (GQLA_DC + GQLA_DR); a.c_inner = GQLA_DC + GQLA_DR;
+  a.c_batch = (int64_t)hpg * (GQLA_DC + GQLA_DR);
+  a.M = n_tokens * hpg; a.N = GQLA_DC; a.K = GQLA_DH; a.batches = h_kv;
+  if (mla::launch_gemm(a, stream) != hipSuccess) return MLA_ERR_HIP;
+  mla::Cols64Args r = {};
+  r.src = (const uint16_t*)q; r.dst = (uint16_t*)q_absorbed;
+  r.rows = (int64_t)n_tokens * h_q; r.reps = 1;
+  r.src_stride = GQLA_DQ; r.src_off = GQLA_DH;
+  r.dst_stride = GQLA_DC + GQLA_DR; r.dst_off = GQLA_DC;
+  return mla::launch_copy_cols64(r, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int gqla_absorb_output(const void* o_latent, const void* w_uv, void* out, int32_t n_tokens,
+                       int32_t h_q, int32_t h_kv, hipStream_t stream) {
+  int rc;
+  if ((rc = gqla_heads(n_tokens, h_q, h_kv)) != MLA_OK) return rc;
+  if (n_tokens == 0) return MLA_OK;
+  if (!o_latent || !w_uv || !out) return MLA_ERR_NULL_ARG;
+  if (!aligned16(o_latent) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_BAD_SHAPE;
+  const int hpg = h_q / h_kv;
+  mla::GemmArgs a = {};
+  a.a = (const uint16_t*)o_latent;
+  a.inner = hpg;
+  a.a_outer = (int64_t)h_q * GQLA_DC; a.a_inner = GQLA_DC; a.a_batch = (int64_t)hpg * GQLA_DC;
+  a.b = (const uint16_t*)w_uv;  // [c][j]: K rows, N contiguous
+  a.b_batch = (int64_t)GQLA_DC * GQLA_DVG; a.ldb = GQLA_DVG; a.b_kn = 1;
+  a.c = (uint16_t*)out;
+  a.c_outer = (int64_t)h_q * GQLA_DVG; a.c_inner = GQLA_DVG; a.c_batch = (int64_t)hpg * GQLA_DVG;
+  a.M = n_tokens * hpg; a.N = GQLA_DVG; a.K = GQLA_DC; a.batches = h_kv;
+  return mla::launch_gemm(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int gqla_expand_kv(const void* kv_rows, const void* w_uk, const void* w_uv, void* k_rows,
+                   void* v_rows, int64_t n_rows, int32_t h_kv, hipStream_t stream) {
+  if (n_rows < 0 || h_kv < 1 || h_kv > 4096) return MLA_ERR_BAD_SHAPE;
+  if (n_rows > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (n_rows == 0) return MLA_OK;
+  if (!kv_rows || !w_uk || !w_uv || !k_rows || !v_rows) return MLA_ERR_NULL_ARG;
+  if (!aligned16(kv_rows) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(k_rows) ||
+      !aligned16(v_rows))
+    return MLA_ERR_BAD_SHAPE;
+  mla::GemmArgs a = {};
+  a.a = (const uint16_t*)kv_rows;
+  a.inner = 1;
+  a.a_outer = GQLA_DC + GQLA_DR;
+  a.b_batch = (int64_t)GQLA_DC * GQLA_DH; a.ldb = GQLA_DH; a.b_kn = 1;
+  a.M = (int)n_rows; a.N = GQLA_DH; a.K = GQLA_DC; a.batches = h_kv;
+  // K: group g's columns 0..127 of each expanded row
+  a.b = (const uint16_t*)w_uk;
+  a.c = (uint16_t*)k_rows;
+  a.c_outer = (int64_t)h_kv * GQLA_DQ; a.c_batch = GQLA_DQ;
+  if (mla::launch_gemm(a, stream) != hipSuccess) return MLA_ERR_HIP;
+  // V
+  a.b = (const uint16_t*)w_uv;
+  a.b_batch = (int64_t)GQLA_DC * GQLA_DVG; a.ldb = GQLA_DVG; a.N = GQLA_DVG;
+  a.c = (uint16_t*)v_rows;
+  a.c_outer = (int64_t)h_kv * GQLA_DVG; a.c_batch = GQLA_DVG;
+  if (mla::launch_gemm(a, stream) != hipSuccess) return MLA_ERR_HIP;
+  // the shared rope columns into every group's K row
+  mla::Cols64Args r = {};
+  r.src = (const uint16_t*)kv_rows; r.dst = (uint16_t*)k_rows;
+  r.rows = n_rows; r.reps = h_kv;
+  r.src_stride = GQLA_DC + GQLA_DR; r.src_off = GQLA_DC;
+  r.dst_stride = GQLA_DQ; r.dst_off = GQLA_DH;
+  return mla::launch_copy_cols64(r, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q, int32_t h_q,

@@ -57,38 +57,60 @@ __device__ __forceinline__ void decode_block_id(int bid, int W, int RB, int& w, 
 }
 
 // LDS page layouts (bytes). Row k of a page keeps its 16-byte chunk c at
-// k * PITCH + 16 * (c ^ row_xor(k)). Measured on gfx950 (whose LDS serves
-// 256 bytes per clock), these two choices let the K-operand reads (16 rows x
-// 16 bytes per 16-lane group) run at the full LDS rate and the transposed V
-// reads (4 rows x 32 bytes per group) at their best rate; a 3-bit XOR over
-// 1 KiB rows ran both at about half of that.
-template <bool GQA>
+// k * PITCH + 16 * (c ^ xor(k)). Measured on gfx950 (whose LDS serves 256
+// bytes per clock), these choices let the K-operand reads (16 rows x 16 bytes
+// per 16-lane group) run at the full LDS rate and the transposed V reads (4
+// rows x 32 bytes per group) at their best rate; a 3-bit XOR over 1 KiB rows
+// ran both at about half of that. An XOR below 8 keeps a chunk inside its
+// aligned group of 8 chunks (K_XOR8 / V_XOR8), so one lane offset serves
+// every group of a row; a 4-bit XOR needs one offset per chunk position.
+template <int KIND>
 struct Layout;
 
 // Latent cache: a page is copied as it lies in HBM, 64 rows of 1152 bytes:
 // columns 0..511 (latent, which is also V) in chunks 0..63, the rope columns
-// 512..575 in chunks 64..71. The XOR (row & 7) stays inside aligned groups of
-// 8 chunks, so the rope stays in chunks 64..71.
+// 512..575 in chunks 64..71.
 template <>
-struct Layout<false> {
+struct Layout<KIND_MLA> {
   static constexpr int D = 576, DV = 512;
-  static constexpr int PITCH = 1152;
-  static constexpr int TILE = 64 * PITCH;  // one page
+  static constexpr int K_PITCH = 1152, V_PITCH = 1152;
+  static constexpr int TILE = 64 * K_PITCH;  // one page
   static constexpr int V_BASE = 0;
   static constexpr int DMA_PER_TILE = 72;  // 1 KiB per instruction
-  static __device__ __forceinline__ int row_xor(int k) { return k & 7; }
+  static constexpr bool K_XOR8 = true, V_XOR8 = true;
+  static __device__ __forceinline__ int k_xor(int k) { return k & 7; }
+  static __device__ __forceinline__ int v_xor(int k) { return k & 7; }
 };
 
 // GQA: separate 128-wide K and V rows (256 bytes, 16 chunks) of one KV head;
 // the XOR 2 (k & 7) stays inside the row.
 template <>
-struct Layout<true> {
+struct Layout<KIND_GQA> {
   static constexpr int D = 128, DV = 128;
-  static constexpr int PITCH = 256;
-  static constexpr int TILE = 2 * 64 * PITCH;
-  static constexpr int V_BASE = 64 * PITCH;
+  static constexpr int K_PITCH = 256, V_PITCH = 256;
+  static constexpr int TILE = 2 * 64 * 256;
+  static constexpr int V_BASE = 64 * 256;
   static constexpr int DMA_PER_TILE = 32;
-  static __device__ __forceinline__ int row_xor(int k) { return (k & 7) << 1; }
+  static constexpr bool K_XOR8 = false, V_XOR8 = false;
+  static __device__ __forceinline__ int k_xor(int k) { return (k & 7) << 1; }
+  static __device__ __forceinline__ int v_xor(int k) { return (k & 7) << 1; }
+};
+
+// GQA with decoupled rope: 192-wide K rows (128 group columns + the 64 rope
+// columns, 384 bytes = 24 chunks) and 128-wide V rows. A 384-byte pitch puts
+// rows 16 bytes x 8 apart modulo the 256 LDS bytes, as the 1152-byte latent
+// rows are, so K takes the latent layout's XOR and V the GQA one. Two page
+// buffers take 80 KiB: two workgroups share a CU.
+template <>
+struct Layout<KIND_GQA_ROPE> {
+  static constexpr int D = 192, DV = 128;
+  static constexpr int K_PITCH = 384, V_PITCH = 256;
+  static constexpr int TILE = 64 * 384 + 64 * 256;
+  static constexpr int V_BASE = 64 * 384;
+  static constexpr int DMA_PER_TILE = 40;
+  static constexpr bool K_XOR8 = true, V_XOR8 = false;
+  static __device__ __forceinline__ int k_xor(int k) { return k & 7; }
+  static __device__ __forceinline__ int v_xor(int k) { return (k & 7) << 1; }
 };
 
 // Issue one 1 KiB HBM -> LDS copy: lane l's 16 bytes at sbase + voff land at
@@ -154,6 +176,25 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Block-wide OR of a per-lane flag, through the first words of the page
+// buffers. Called only where those are idle: every copy has landed and every
+// wave has passed the page loop's last barrier. (The runtime's own
+// __syncthreads_or keeps 256 bytes of LDS of its own, which would leave the
+// 80 KiB page buffers of the rope layout one workgroup per CU.)
+template <int NW>
+__device__ __forceinline__ bool block_or(bool x, lds_char* lds_p, int wave) {
+  typedef __attribute__((address_space(3))) int lds_int;
+  lds_int* f = (lds_int*)lds_p;
+  const int any = __any(x) ? 1 : 0;
+  if ((threadIdx.x & 63) == 0) f[wave] = any;
+  __syncthreads();
+  int r = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) r |= f[w];
+  __syncthreads();  // the words are page data again afterwards
+  return r != 0;
+}
+
 __device__ __forceinline__ float max4groups(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
@@ -163,9 +204,10 @@ __device__ __forceinline__ float sum4groups(float x) {
   return x + __shfl_xor(x, 32);
 }
 
-template <int R, bool GQA>
+template <int R, int KIND>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-  using LY = Layout<GQA>;
+  using LY = Layout<KIND>;
+  constexpr bool GQA = KIND != KIND_MLA;
   constexpr int NW = 4;
   constexpr int KS = NW / R;      // waves sharing a row group (key split)
   constexpr int KW = 64 / KS;     // keys per wave per page
@@ -209,28 +251,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   // ---- per-lane LDS offsets (bytes, relative to a page buffer) ----
   // Score operand: key ks*KW + 16kb + n, K step c covers columns 32c .. 32c+31,
-  // of which this lane reads chunk 4c + g4. MLA: the XOR (< 8) leaves the
-  // 8-chunk group alone, so two offsets (c even / odd) plus 128 (c >> 1)
-  // cover all 18 steps, rope included. GQA: the 4-bit XOR reaches across the
-  // group, so each of the 4 steps has its own offset.
-  constexpr int NQO = GQA ? 4 : 2;
-  const int xn = LY::row_xor(n);
+  // of which this lane reads chunk 4c + g4. With an XOR below 8 the 8-chunk
+  // group stays put, so two offsets (c even / odd) plus 128 (c >> 1) cover
+  // every step, rope included; the 4-bit XOR reaches across the group, so
+  // each step has its own offset.
+  constexpr int NQO = LY::K_XOR8 ? 2 : 4;
+  const int xn = LY::k_xor(n);
   uint32_t qk_off[NQO];
 #pragma unroll
   for (int q = 0; q < NQO; ++q)
-    qk_off[q] = (ks * KW + n) * LY::PITCH + 16 * ((4 * q + g4) ^ xn);
+    qk_off[q] = (ks * KW + n) * LY::K_PITCH + 16 * ((4 * q + g4) ^ xn);
   // V^T operand by transposed reads: 16-lane group g4 reads keys
   // 4*g4 + (j>>2) (+ a multiple of 16) at columns 16cb + 4(j&3) .. +3, i.e.
-  // chunk 2cb + (j&3)/2; MLA needs 4 offsets (cb & 3) plus 128 (cb >> 2),
-  // GQA one per column block.
-  constexpr int NVO = GQA ? 8 : 4;
+  // chunk 2cb + (j&3)/2; with an XOR below 8, 4 offsets (cb & 3) plus 128
+  // (cb >> 2), else one per column block.
+  constexpr int NVO = LY::V_XOR8 ? 4 : 8;
   const int j16 = lane & 15;
   const int vkey = 4 * g4 + (j16 >> 2);
-  const int xv = LY::row_xor(vkey);
+  const int xv = LY::v_xor(vkey);
   uint32_t v_off[NVO];
 #pragma unroll
   for (int q = 0; q < NVO; ++q)
-    v_off[q] = LY::V_BASE + (ks * KW + vkey) * LY::PITCH +
+    v_off[q] = LY::V_BASE + (ks * KW + vkey) * LY::V_PITCH +
                16 * ((2 * q + ((j16 & 3) >> 1)) ^ xv) + 8 * (j16 & 1);
 
   for (int b = bs; b <= be; ++b) {
@@ -269,21 +311,34 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           const int i = wave + NW * t;
           const int u = 64 * i + lane;
           const int r = u / 72, x = u - 72 * r;
-          const uint32_t vo = min(r, nv - 1) * LY::PITCH + 16 * (x ^ LY::row_xor(r));
+          const uint32_t vo = min(r, nv - 1) * LY::K_PITCH + 16 * (x ^ LY::k_xor(r));
           dma16(dst + 1024 * i, pbase, vo);
         }
       } else {
-        const uint32_t rstride = (uint32_t)a.G * 256;  // bytes between tokens
-        const size_t pg = ((size_t)page * 64 * a.G + g) * 256;
-        const char* kbase = uniform_ptr((const char*)a.k + pg);
-        const char* vbase = uniform_ptr((const char*)a.v + pg);
+        // KV head g's rows of the page: K rows of KC16 chunks, V rows of VC16
+        // chunks, tokens G heads apart in HBM; copy i of K (or V) holds
+        // 16-byte units u = 64i + lane, chunk x of row r, as above
+        constexpr int KC16 = LY::D / 8, VC16 = LY::DV / 8;
+        static_assert(KC16 % NW == 0 && VC16 % NW == 0, "copies split evenly");
+        const uint32_t kstride = (uint32_t)a.G * (LY::D * 2);  // bytes between tokens
+        const uint32_t vstride = (uint32_t)a.G * (LY::DV * 2);
+        const size_t row0 = (size_t)page * 64 * a.G + g;
+        const char* kbase = uniform_ptr((const char*)a.k + row0 * (LY::D * 2));
+        const char* vbase = uniform_ptr((const char*)a.v + row0 * (LY::DV * 2));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ii = wave + NW * i;  // rows 4ii .. 4ii+3
-          const int k = 4 * ii + (lane >> 4);
-          const uint32_t vo = min(k, nv - 1) * rstride + 16 * ((lane & 15) ^ LY::row_xor(k));
-          dma16(dst + ii * 1024, kbase, vo);
-          dma16(dst + LY::V_BASE + ii * 1024, vbase, vo);
+        for (int t = 0; t < KC16 / NW; ++t) {
+          const int i = wave + NW * t;
+          const int u = 64 * i + lane;
+          const int r = u / KC16, x = u - KC16 * r;
+          dma16(dst + 1024 * i, kbase, min(r, nv - 1) * kstride + 16 * (x ^ LY::k_xor(r)));
+        }
+#pragma unroll
+        for (int t = 0; t < VC16 / NW; ++t) {
+          const int i = wave + NW * t;
+          const int u = 64 * i + lane;
+          const int r = u / VC16, x = u - VC16 * r;
+          dma16(dst + LY::V_BASE + 1024 * i, vbase,
+                min(r, nv - 1) * vstride + 16 * (x ^ LY::v_xor(r)));
         }
       }
     };
@@ -351,8 +406,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       // ahead of the MFMA that uses them.
       auto k_frag = [&](int st) -> bf16x8 {
         const int c = st / KB, kb = st % KB;
-        const lds_char* p = GQA ? kp[c % NQO] + kb * 16 * LY::PITCH
-                                : kp[c & 1] + kb * 16 * LY::PITCH + 128 * (c >> 1);
+        const lds_char* p = LY::K_XOR8 ? kp[c & 1] + kb * 16 * LY::K_PITCH + 128 * (c >> 1)
+                                       : kp[c % NQO] + kb * 16 * LY::K_PITCH;
         return *(const __attribute__((address_space(3))) bf16x8*)p;
       };
       constexpr int NQK = KB * KC;
@@ -443,11 +498,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         // hit different output blocks; V^T fragments are read PF steps ahead
         auto v_frag = [&](int st) -> bf16x8 {
           const int c = st / NCB, cb = st % NCB;
-          const lds_char* p = (32 * c) * LY::PITCH +
-                              (GQA ? vp[cb % NVO] : vp[cb & 3] + 128 * (cb >> 2));
+          const lds_char* p = (32 * c) * LY::V_PITCH +
+                              (LY::V_XOR8 ? vp[cb & 3] + 128 * (cb >> 2) : vp[cb % NVO]);
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
           const bf16x4 hi =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * LY::PITCH));
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * LY::V_PITCH));
           return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         constexpr int NST = NCB * PC;
@@ -469,7 +524,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         px[1] = pack_bf16x2(s[0][2], s[0][3]);
         const bf16x4 pf = __builtin_bit_cast(bf16x4, px);
         auto v_frag = [&](int cb) -> bf16x4 {
-          const lds_char* p = GQA ? vp[cb % NVO] : vp[cb & 3] + 128 * (cb >> 2);
+          const lds_char* p = LY::V_XOR8 ? vp[cb & 3] + 128 * (cb >> 2) : vp[cb % NVO];
           return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
         };
         constexpr int PFV = NCB < PF ? NCB : PF;
@@ -488,7 +543,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     return over;
     };
     // every wave runs the same passes: the page buffers and barriers are shared
-    if (__syncthreads_or(run_range(std::true_type{}))) run_range(std::false_type{});
+    if (block_or<NW>(run_range(std::true_type{}), lds_p, wave)) run_range(std::false_type{});
 
     // merge the key parts of each row group through LDS (page buffers are
     // free: every copy has landed and every wave has passed the last barrier)
@@ -549,26 +604,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 }
 
-template <int R, bool GQA>
+template <int R, int KIND>
 static hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<R, GQA>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_kernel<R, KIND>), dim3(grid), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_kernel(const DecodeArgs& a, int row_groups, bool gqa, int grid,
+template <int KIND>
+static hipError_t launch_kind(const DecodeArgs& a, int row_groups, int grid, hipStream_t st) {
+  switch (row_groups) {
+    case 1: return launch_decode<1, KIND>(a, grid, st);
+    case 2: return launch_decode<2, KIND>(a, grid, st);
+    case 4: return launch_decode<4, KIND>(a, grid, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_kernel(const DecodeArgs& a, int row_groups, int kind, int grid,
                                 hipStream_t st) {
-  if (!gqa) {
-    switch (row_groups) {
-      case 1: return launch_decode<1, false>(a, grid, st);
-      case 2: return launch_decode<2, false>(a, grid, st);
-      case 4: return launch_decode<4, false>(a, grid, st);
-    }
-  } else {
-    switch (row_groups) {
-      case 1: return launch_decode<1, true>(a, grid, st);
-      case 2: return launch_decode<2, true>(a, grid, st);
-      case 4: return launch_decode<4, true>(a, grid, st);
-    }
+  switch (kind) {
+    case KIND_MLA: return launch_kind<KIND_MLA>(a, row_groups, grid, st);
+    case KIND_GQA: return launch_kind<KIND_GQA>(a, row_groups, grid, st);
+    case KIND_GQA_ROPE: return launch_kind<KIND_GQA_ROPE>(a, row_groups, grid, st);
   }
   return hipErrorInvalidValue;
 }

@@ -6,6 +6,13 @@
 
 namespace mla {
 
+// Cache shapes of the decode kernel.
+enum : int {
+  KIND_MLA = 0,       // latent rows of 576 (V = the first 512 columns), one KV head
+  KIND_GQA = 1,       // separate 128-wide K and V rows per KV head
+  KIND_GQA_ROPE = 2,  // 192-wide K rows (128 + 64 rope) and 128-wide V rows per KV head
+};
+
 struct DecodeArgs {
   const uint16_t* q;           // [B, T, H, D]
   const uint16_t* k;           // [P, 64, G, D]
@@ -46,11 +53,39 @@ struct AppendArgs {
   int B, T, bt_stride, num_pages;
 };
 
+// C = A . B on bf16 MFMA with fp32 accumulation, rounded to bf16, for a
+// batch of problems (blockIdx.y). Row m of A (and of C) in problem z starts
+// at  base + z * batch + (m / inner) * outer + (m % inner) * inner_stride
+// (elements); rows hold K (A) or N (C) contiguous elements. B of problem z
+// starts at b + z * b_batch and is [N][ldb] with K contiguous (b_kn = 0) or
+// [K][ldb] with N contiguous (b_kn = 1). N % 128 == 0, K % 64 == 0.
+struct GemmArgs {
+  const uint16_t* a;
+  const uint16_t* b;
+  uint16_t* c;
+  int64_t a_outer, a_inner, a_batch;
+  int64_t b_batch;
+  int64_t c_outer, c_inner, c_batch;
+  int ldb, inner, M, N, K, batches, b_kn;
+};
+
+// dst[(r * reps + j) * dst_stride + dst_off + e] = src[r * src_stride + src_off + e]
+// for r < rows, j < reps, e < 64 (bf16 elements, 16-byte aligned runs).
+struct Cols64Args {
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t rows, src_stride, dst_stride;
+  int reps, src_off, dst_off;
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_copy_cols64(const Cols64Args& a, hipStream_t st);
+
 // Paged KV append: one wave per new token.
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t st);
 
 // One decode launch: grid = workers * row blocks, 64 * nw threads.
-hipError_t launch_decode_kernel(const DecodeArgs& a, int nw, bool gqa, int grid, hipStream_t st);
+hipError_t launch_decode_kernel(const DecodeArgs& a, int nw, int kind, int grid, hipStream_t st);
 // Split-KV merge of the partial results of split sequences.
 hipError_t launch_combine_kernel(const CombineArgs& a, hipStream_t st);
 // Schedule: worker records and unit prefix into meta, slot prefix into slots.

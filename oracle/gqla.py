@@ -25,6 +25,10 @@ Readings where the pages give no formulas (each listed in the design notes):
   * The output projection after attention is not part of this step.
 In exact arithmetic both paths equal the direct definition; here all three
 are evaluated in float64 from the bf16 inputs, with no rounding in between.
+With ``round_bf16=True`` a path instead rounds its stored intermediates to
+bf16 (nearest-even, by way of float32) where a bf16 implementation stores
+them: the absorbed query and the latent attention output (absorb path), the
+expanded K and V rows (GQA path); everything else stays float64.
 
 Inputs: bf16 bit patterns as uint16 numpy arrays — q [B, T, H, d_h + d_r],
 kv [P, 64, 1, d_c + d_r], w_uk [G, d_c, d_h], w_uv [G, d_c, d_v] — plus int32
@@ -37,6 +41,15 @@ import numpy as np
 from .attention import bf16_to_f64, gather_pages, scale_as_received, visible_keys
 
 D_C, D_R = 512, 64
+
+
+def round_bf16(x):
+    """float64 values rounded to float32 (nearest-even) and then to bf16
+    (nearest-even on the top 16 bits of the float32 pattern), returned as
+    float64. Finite inputs only."""
+    u = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def _groups(H, G):
@@ -142,13 +155,14 @@ def attend_direct(q, kv, w_uk, w_uv, block_table, seqlens, scale, causal):
     return out, lse
 
 
-def attend_absorb(q, kv, w_uk, w_uv, block_table, seqlens, scale, causal):
+def attend_absorb(q, kv, w_uk, w_uv, block_table, seqlens, scale, causal, round_bf16=False):
     """The MQA-absorb path: absorbed queries attend the 576-wide latent rows
     with the latent c as values, and the result is multiplied by W_UV^g.
     Returns (out [B, T, H, d_v], lse [B, T, H], o_latent [B, T, H, d_c])."""
+    rnd = globals()["round_bf16"] if round_bf16 else (lambda x: x)
     B, T, H, _ = q.shape
     sigma = scale_as_received(scale)
-    qa = absorb_query(q, w_uk)
+    qa = rnd(absorb_query(q, w_uk))
     o_lat = np.zeros((B, T, H, D_C))
     lse = np.full((B, T, H), -np.inf)
     for b in range(B):
@@ -159,13 +173,22 @@ def attend_absorb(q, kv, w_uk, w_uv, block_table, seqlens, scale, causal):
         for t in range(T):
             vis = [visible_keys(L, T, t, causal)] * H
             o_lat[b, t], lse[b, t] = _attend(qa[b, t], lat, lat[:, :D_C], sigma, vis)
+    o_lat = rnd(o_lat)
     return absorb_output(o_lat, w_uv), lse, o_lat
 
 
-def attend_gqa_path(q, kv, w_uk, w_uv, block_table, seqlens, scale, causal):
-    """The GQA path: expand the whole cache per group, then grouped attention
-    of the unchanged queries over the expanded pages. Returns out, lse."""
-    K, V = expand_group_cache(kv, w_uk, w_uv)
+def attend_gqa_path(q, kv, w_uk, w_uv, block_table, seqlens, scale, causal, round_bf16=False,
+                    pages=None):
+    """The GQA path: expand the cache per group, then grouped attention of
+    the unchanged queries over the expanded pages. ``pages`` limits the
+    expansion to the physical pages the given sequences use (the rest of the
+    pool is never read). Returns out, lse."""
+    idx = (np.arange(kv.shape[0]) if pages is None
+           else np.asarray(sorted(set(int(p) for p in pages)), dtype=np.int64))
+    K, V = expand_group_cache(kv[idx], w_uk, w_uv)   # rows of the listed pages only
+    at = {int(p): i for i, p in enumerate(idx)}
+    if round_bf16:
+        K, V = globals()["round_bf16"](K), globals()["round_bf16"](V)
     B, T, H, _ = q.shape
     G = K.shape[2]
     hpg = _groups(H, G)
@@ -178,9 +201,9 @@ def attend_gqa_path(q, kv, w_uk, w_uv, block_table, seqlens, scale, causal):
         if L <= 0:
             continue
         n = (L + 63) // 64
-        pages = [int(p) for p in block_table[b, :n]]
-        Kb = np.concatenate([K[p] for p in pages], axis=0)[:L]   # [L, G, D]
-        Vb = np.concatenate([V[p] for p in pages], axis=0)[:L]
+        rows = [at[int(p)] for p in block_table[b, :n]]
+        Kb = np.concatenate([K[i] for i in rows], axis=0)[:L]   # [L, G, D]
+        Vb = np.concatenate([V[i] for i in rows], axis=0)[:L]
         for g in range(G):
             hs = slice(g * hpg, (g + 1) * hpg)
             for t in range(T):

@@ -20,7 +20,8 @@ def L():
 def test_every_declared_function_is_exported(L):
     names = _lib.header_functions()
     assert {"mla_decode_plan", "mla_decode", "gqa_decode", "attn_combine", "mla_kv_append",
-            "gqa_kv_append"} <= set(names)
+            "gqa_kv_append", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output",
+            "gqla_decode"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -99,6 +100,30 @@ def test_kv_append_argument_checks(L):
     assert L.gqa_kv_append(p, p, p, None, p, p, 2, 1, 8, 4, 4, None) == -1
     assert L.gqa_kv_append(p, p, p, p, p, p, 2, 1, 0, 4, 4, None) == -2
     assert L.gqa_kv_append(p, p, p, p, p, p, 0, 1, 8, 4, 4, None) == 0
+
+
+def test_gqla_argument_checks(L):
+    p = ctypes.c_void_p(64)
+    # q, w_uk, q_absorbed, n_tokens, h_q, h_kv
+    assert L.gqla_absorb_query(p, p, p, 0, 16, 4, None) == 0          # nothing to do
+    assert L.gqla_absorb_query(None, p, p, 2, 16, 4, None) == -1
+    assert L.gqla_absorb_query(p, p, None, 2, 16, 4, None) == -1
+    assert L.gqla_absorb_query(p, p, p, 2, 16, 5, None) == -2        # 16 heads, 5 groups
+    assert L.gqla_absorb_query(p, p, p, -1, 16, 4, None) == -2
+    assert L.gqla_absorb_query(ctypes.c_void_p(72), p, p, 2, 16, 4, None) == -2
+    assert L.gqla_absorb_query(p, p, p, 1 << 30, 16, 1, None) == -3
+    assert L.gqla_absorb_output(p, None, p, 2, 16, 4, None) == -1
+    assert L.gqla_absorb_output(p, p, p, 2, 0, 1, None) == -2
+    # kv_rows, w_uk, w_uv, k_rows, v_rows, n_rows, h_kv
+    assert L.gqla_expand_kv(p, p, p, p, p, 0, 8, None) == 0
+    assert L.gqla_expand_kv(p, p, None, p, p, 64, 8, None) == -1
+    assert L.gqla_expand_kv(p, p, p, p, p, 64, 0, None) == -2
+    assert L.gqla_expand_kv(p, p, p, p, p, -1, 8, None) == -2
+    assert L.gqla_expand_kv(p, p, p, p, p, 1 << 31, 8, None) == -3
+    rc = L.gqla_decode(p, p, None, p, p, 2, 1, 16, 4, 3, 4, 0.1, 0, p, p, None, 0, p, p, None)
+    assert rc == -1  # no V cache
+    rc = L.gqla_decode(p, p, p, p, p, 2, 1, 12, 5, 3, 4, 0.1, 0, p, p, None, 0, p, p, None)
+    assert rc == -2
 
 
 # ------------------------------------------------------------ the schedule

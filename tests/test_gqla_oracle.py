@@ -170,3 +170,55 @@ def test_rows_without_keys_are_zero_with_minus_infinite_lse():
         # causal, s_q = 2: the first query token of the 1-token sequence sees nothing
         assert np.all(out[1, 0] == 0.0) and np.all(lse[1, 0] == -np.inf)
         assert np.isfinite(lse[1, 1]).all()
+
+
+def test_bf16_rounding_is_nearest_even():
+    one = 1.0
+    x = np.array([one, one + 2.0 ** -8, one + 3 * 2.0 ** -8, one + 2.0 ** -8 + 2.0 ** -20,
+                  -2.5, 3.0e38, 2.0 ** -130, 2.0 ** -140, one + 2.0 ** -8 + 2.0 ** -30])
+    r = gqla.round_bf16(x)
+    assert r[0] == 1.0
+    assert r[1] == 1.0                       # tie -> even (significand ...0)
+    assert r[2] == 1.0 + 2.0 ** -6           # tie -> even (significand ...10)
+    assert r[3] == 1.0 + 2.0 ** -7           # above the tie -> up
+    assert r[4] == -2.5
+    assert r[5] == 2.0 ** 127 * 226 / 128   # 3e38 / 2^127 = 1.7632 -> 226 / 128
+    assert r[6] == 2.0 ** -130               # a bf16 subnormal, exact
+    assert r[7] == 0.0                       # below half the smallest bf16 subnormal (2^-133)
+    assert r[8] == 1.0                       # float32 first: the 2^-30 is lost, then a tie
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal(1000) * 10.0 ** rng.uniform(-5, 5, 1000)
+    ry = gqla.round_bf16(y)
+    assert np.all(np.abs(ry - y) <= oracle.bf16_step(y) / 2 * (1 + 1e-12))
+
+
+def test_rounding_points_change_nothing_for_exact_bf16_intermediates():
+    """With column-selecting weights every intermediate of both paths is a
+    bf16 value already, except the latent attention output; with a single key
+    that output is a latent row itself."""
+    d = _small(seqlens_fixed=(1, 1, 1), causal=False, s_q=1)
+    G = d["cfg"].h_kv
+    d["w_uk"] = _selection(G, 128, [0, 128, 256, 384])
+    d["w_uv"] = _selection(G, 128, [384, 0, 64, 200])
+    ex = _run(gqla.attend_direct, d)
+    c = d["cfg"]
+    args = (d["q"], d["kv"], d["w_uk"], d["w_uv"], d["block_table"], d["cache_seqlens"],
+            c.scale, c.causal)
+    a_out, a_lse, _ = gqla.attend_absorb(*args, round_bf16=True)
+    g_out, g_lse = gqla.attend_gqa_path(*args, round_bf16=True)
+    for o, l in ((a_out, a_lse), (g_out, g_lse)):
+        _close(o, ex[0])
+        _close(l, ex[1])
+
+
+def test_gqa_path_restricted_to_used_pages_is_unchanged():
+    d = _small()
+    c = d["cfg"]
+    args = (d["q"], d["kv"], d["w_uk"], d["w_uv"], d["block_table"], d["cache_seqlens"],
+            c.scale, c.causal)
+    full = gqla.attend_gqa_path(*args)
+    bt = d["block_table"]
+    used = [int(p) for p in bt[bt >= 0]]
+    part = gqla.attend_gqa_path(*args, pages=used)
+    _close(part[0], full[0], rel=0)
+    _close(part[1], full[1], rel=0)
