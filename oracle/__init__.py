@@ -7,11 +7,11 @@ a library routine; none is marked "parity unpinned".
 """
 from .tolerance import compare, bf16_step
 from .append import append_rows, new_token_slots
-from . import gqla
+from . import gqla, fp8
 from .attention import (PAGE, attend_bruteforce, attend_online, attend_two_pass,
                         bf16_to_f64, combine, gather_pages, scale_as_received,
                         softmax_weights, visible_keys)
 
-__all__ = ["gqla", "compare", "bf16_step", "append_rows", "new_token_slots", "PAGE", "attend_bruteforce", "attend_online", "attend_two_pass",
+__all__ = ["gqla", "fp8", "compare", "bf16_step", "append_rows", "new_token_slots", "PAGE", "attend_bruteforce", "attend_online", "attend_two_pass",
            "bf16_to_f64", "combine", "gather_pages", "scale_as_received",
            "softmax_weights", "visible_keys"]
