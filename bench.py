@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
     python bench.py --op append [--config N] [--append-tokens T]
     python bench.py --op gqla
+    python bench.py --kv fp8 [--config 2|3|4]    (MLA decode over an FP8 latent cache)
 
 
 One step is the whole path over one batch: the split-KV plan, the fused
@@ -40,13 +41,16 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "mla_paged_kv_03_amd", "csrc", "decode_kernels.hip")
 
 
-def algorithmic_work(d):
+def algorithmic_work(d, fp8=False):
     """Bytes and FLOPs an IO-optimal decode must move and compute: every
-    valid cached token once, q, out and lse; 2 (d_qk + d_v) flop per
-    (query row, visible key) pair."""
+    valid cached token once (an FP8 latent row: 576 code bytes + a 4-byte
+    scale), q, out and lse; 2 (d_qk + d_v) flop per (query row, visible
+    key) pair."""
     cfg = d["cfg"]
     L = d["cache_seqlens"].astype(np.int64)
     tok_bytes = cfg.h_kv * (cfg.d_qk * 2 if cfg.kind == "mla" else (cfg.d_qk + cfg.d_v) * 2)
+    if fp8:
+        tok_bytes = cfg.d_qk + 4
     rows = cfg.batch * cfg.s_q * cfg.h_q
     kv = int(L.sum()) * tok_bytes
     qb = rows * cfg.d_qk * 2
@@ -357,6 +361,9 @@ def main():
     ap.add_argument("--op", choices=["decode", "append", "gqla"], default="decode",
                     help="decode (the default step), the paged KV append alone, or GQLA's "
                          "two decode paths")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="latent cache format for the MLA configs (fp8: E4M3 codes with a "
+                         "per-token scale, quantised on the GPU before the timed region)")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="new tokens per sequence for --op append (default: the config's s_q)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -384,6 +391,10 @@ def main():
     from workloads import CONFIGS, make_inputs
 
     cfg = CONFIGS[args.config]
+    fp8 = args.kv == "fp8"
+    if fp8 and cfg.kind != "mla":
+        print("bench.py: --kv fp8 applies to the MLA configs (1-4)", file=sys.stderr)
+        sys.exit(2)
     if args.op == "gqla":
         bench_gqla(args)
         return
@@ -403,12 +414,14 @@ def main():
         for k in ("kv", "k", "v"):
             if k in d:
                 t[k] = torch.from_numpy(d[k].view(np.int16)).view(torch.bfloat16).to(dev)
+        if fp8:
+            t["codes"], t["scales"] = lib.mla_kv_quantize_fp8(t.pop("kv"))
         sets.append((d, t))
         if r > 0:
             for k in ("kv", "k", "v"):
                 d.pop(k, None)  # the first set's host copy serves the CPU baseline
     d0 = sets[0][0]
-    work = algorithmic_work(d0)
+    work = algorithmic_work(d0, fp8)
     B, T, H, G = cfg.batch, cfg.s_q, cfg.h_q, cfg.h_kv
     dv = cfg.d_v
     plan = lib.mla_decode_plan(sets[0][1]["sl"], T, H, G, dv)
@@ -426,7 +439,12 @@ def main():
                                P(plan.num_splits), pinfo, stream)
         if rc:
             raise lib.DecodeError("mla_decode_plan", rc)
-        if cfg.kind == "mla":
+        if fp8:
+            rc = L.mla_decode_fp8(P(t["q"]), P(t["codes"]), P(t["scales"]), P(t["bt"]), P(t["sl"]),
+                                  B, T, H, t["codes"].shape[0], t["bt"].shape[1], cfg.scale,
+                                  int(cfg.causal), P(plan.sched_metadata), P(plan.num_splits),
+                                  ws, wsb, P(out), P(lse), stream)
+        elif cfg.kind == "mla":
             rc = L.mla_decode(P(t["q"]), P(t["kv"]), P(t["bt"]), P(t["sl"]), B, T, H,
                               t["kv"].shape[0], t["bt"].shape[1], cfg.scale, int(cfg.causal),
                               P(plan.sched_metadata), P(plan.num_splits), ws, wsb, P(out),
@@ -494,7 +512,7 @@ def main():
     gbs = work["bytes"] / s / 1e9
     k_gbs = work["bytes"] / (kern_avg * 1e-3) / 1e9
     k_tflops = work["flops"] / (kern_avg * 1e-3) / 1e12
-    traffic = stored_traffic()
+    traffic = None if fp8 else stored_traffic()
     bound = "hbm" if work["flops"] / work["bytes"] < MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 \
         else "mfma"
     if bound == "hbm":
@@ -504,7 +522,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic}
-    roof["kernel"] = f"decode_kernel ({'gqa' if cfg.kind == 'gqa' else 'mla'})"
+    roof["kernel"] = f"decode_kernel ({'gqa' if cfg.kind == 'gqa' else 'mla fp8' if fp8 else 'mla'})"
     roof["kernel_avg_us"] = round(kern_avg * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = work["bytes"]
     roof["algorithmic_flops_per_launch"] = work["flops"]
@@ -520,9 +538,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 e4m3 cache, bf16 MFMA" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": B, "s_q": T, "h_q": H, "h_kv": G,
+        "config": {"workload": cfg.name + ("_fp8kv" if fp8 else ""), "batch": B, "s_q": T, "h_q": H, "h_kv": G,
                    "d_qk": cfg.d_qk, "d_v": dv, "page": 64, "causal": cfg.causal,
                    "seqlen_total": int(d0["cache_seqlens"].sum()),
                    "workers": info.num_workers, "input_sets_rotated": args.rotate},
@@ -532,7 +550,7 @@ def main():
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "roofline": roof,
     }
-    if not args.no_cpu:
+    if not args.no_cpu and not fp8:
         res["cpu_baseline"] = cpu_baseline(d0)
     print(json.dumps(res), flush=True)
 

@@ -195,6 +195,51 @@ int gqa_kv_append(const void* new_k, const void* new_v, void* k_cache, void* v_c
                   int32_t s_q, int32_t h_kv, int32_t num_pages, int32_t max_pages_per_seq,
                   hipStream_t stream);
 
+/* ---- FP8 latent cache ----
+ *
+ * The pages name FP8 only as FlashAttention-3's low-precision mode
+ * (FlashAttention (KO), "FlashAttention-3 (2024)"); the format here is this
+ * library's: per cached token, 576 OCP E4M3 codes (sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; largest finite value 448; no infinities)
+ * and one fp32 scale, value = e4m3(code) * scale, in two arrays:
+ *   kv_codes   uint8 [num_pages, 64, 576]  (16-byte aligned)
+ *   kv_scales  fp32  [num_pages, 64]       (4-byte aligned)
+ * Quantising a bf16 row x: amax = max |x|; scale = the smallest power of
+ * two not below the fp32 quotient amax / 448, at least 2^-126 (1 for an
+ * all-zero row), a power-of-two scale as in the OCP microscaling formats;
+ * code = the E4M3 value nearest to clamp(x / scale, -448, 448), ties to
+ * even (x / scale is exact). Half the bytes of the bf16 cache (580 against
+ * 1152 per token).
+ */
+
+/* MLA decode over an FP8 latent cache: as mla_decode, with V = the first
+ * 512 dequantised columns. The plan comes from mla_decode_plan with h_kv = 1
+ * and head_dim_v = 512. Errors as for mla_decode, plus MLA_ERR_NULL_ARG for
+ * kv_scales = NULL and MLA_ERR_BAD_SHAPE for a misaligned kv_scales. */
+int mla_decode_fp8(const void* q, const void* kv_codes, const float* kv_scales,
+                   const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                   int32_t s_q, int32_t h_q, int32_t num_pages, int32_t max_pages_per_seq,
+                   float softmax_scale, int32_t causal, const int32_t* sched_metadata,
+                   const int32_t* num_splits, void* workspace, size_t workspace_bytes, void* out,
+                   float* lse, hipStream_t stream);
+
+/* Paged KV append into an FP8 cache: each of the s_q new tokens' bf16 rows
+ * (new_kv [batch, s_q, 576]) is quantised into its slot (same slot rule,
+ * skips and errors as mla_kv_append). Bit-exact: the codes and the scale
+ * are what the rule above gives in fp32. */
+int mla_kv_append_fp8(const void* new_kv, void* kv_codes, float* kv_scales,
+                      const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                      int32_t s_q, int32_t num_pages, int32_t max_pages_per_seq,
+                      hipStream_t stream);
+
+/* Quantise n_rows bf16 latent rows (kv_rows [n_rows, 576], e.g. a whole
+ * cache [num_pages, 64, 1, 576]) into kv_codes [n_rows, 576] and kv_scales
+ * [n_rows] row for row. Errors: MLA_ERR_BAD_SHAPE for n_rows < 0 or
+ * misaligned arrays, MLA_ERR_UNSUPPORTED past 2^31 - 1 rows,
+ * MLA_ERR_NULL_ARG for a NULL pointer when n_rows > 0. */
+int mla_kv_quantize_fp8(const void* kv_rows, void* kv_codes, float* kv_scales, int64_t n_rows,
+                        hipStream_t stream);
+
 /* ---- GQLA: one set of group-indexed weights, two decode paths ----
  *
  * GQLA (GQLA review, "2. Motivation & Problem Statement" and Figure 2) keeps

@@ -21,7 +21,7 @@ from ._lib import DecodeError, PlanInfo
 
 __all__ = ["Plan", "PlanInfo", "DecodeError", "plan_info", "mla_decode_plan", "mla_decode",
            "gqa_decode", "attn_combine", "mla_kv_append", "gqa_kv_append",
-           "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output", "gqla_decode",
+           "mla_decode_fp8", "mla_kv_append_fp8", "mla_kv_quantize_fp8", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output", "gqla_decode",
            "mla_decode_plan_host", "profile_events"]
 
 MLA_D, MLA_DV = 576, 512
@@ -196,6 +196,87 @@ def gqa_kv_append(new_k, new_v, k_cache, v_cache, block_table, cache_seqlens):
         _ptr(new_k), _ptr(new_v), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
         _ptr(cache_seqlens), B, T, G, P, block_table.shape[1], _stream()))
     return k_cache, v_cache
+
+
+def mla_kv_quantize_fp8(kv_rows, codes=None, scales=None):
+    """Quantise bf16 latent rows (kv_rows [..., 576], e.g. a cache
+    [P, 64, 1, 576]) to E4M3 codes uint8 [..., 576] and one fp32 scale per
+    row [...] (a trailing 1 of the leading dims dropped)."""
+    _need(kv_rows, "kv_rows", torch.bfloat16)
+    if kv_rows.shape[-1] != MLA_D:
+        raise ValueError("kv_rows must end in 576 columns")
+    lead = tuple(kv_rows.shape[:-1])
+    if len(lead) >= 2 and lead[-1] == 1:
+        lead = lead[:-1]
+    n = kv_rows.numel() // MLA_D
+    if codes is None:
+        codes = torch.empty(lead + (MLA_D,), dtype=torch.uint8, device=kv_rows.device)
+    if scales is None:
+        scales = torch.empty(lead, dtype=torch.float32, device=kv_rows.device)
+    _need(codes, "codes", torch.uint8)
+    _need(scales, "scales", torch.float32)
+    if codes.numel() != n * MLA_D or scales.numel() != n:
+        raise ValueError("codes / scales do not match kv_rows")
+    _lib.check("mla_kv_quantize_fp8", _lib.lib().mla_kv_quantize_fp8(
+        _ptr(kv_rows), _ptr(codes), _ptr(scales), n, _stream()))
+    return codes, scales
+
+
+def _fp8_cache(kv_codes, kv_scales):
+    _need(kv_codes, "kv_codes", torch.uint8, 3)
+    _need(kv_scales, "kv_scales", torch.float32, 2)
+    P = kv_codes.shape[0]
+    if tuple(kv_codes.shape) != (P, 64, MLA_D) or tuple(kv_scales.shape) != (P, 64):
+        raise ValueError("an FP8 cache is kv_codes uint8 [P, 64, 576] and kv_scales fp32 [P, 64]")
+    return P
+
+
+def mla_kv_append_fp8(new_kv, kv_codes, kv_scales, block_table, cache_seqlens):
+    """Quantise the s_q new tokens' rows (new_kv bf16 [B, s_q, 576]) into
+    their slots of an FP8 cache, in place (slot rule of mla_kv_append)."""
+    _need(new_kv, "new_kv", torch.bfloat16, 3)
+    P = _fp8_cache(kv_codes, kv_scales)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, T, D = new_kv.shape
+    if D != MLA_D or block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("mla_kv_append_fp8 expects new_kv [B, s_q, 576] and B block-table rows")
+    _lib.check("mla_kv_append_fp8", _lib.lib().mla_kv_append_fp8(
+        _ptr(new_kv), _ptr(kv_codes), _ptr(kv_scales), _ptr(block_table), _ptr(cache_seqlens),
+        B, T, P, block_table.shape[1], _stream()))
+    return kv_codes, kv_scales
+
+
+def mla_decode_fp8(q, kv_codes, kv_scales, block_table, cache_seqlens, softmax_scale,
+                   causal=False, plan: Plan | None = None, out=None, lse=None):
+    """MLA decode over an FP8 latent cache (kv_codes uint8 [P, 64, 576],
+    kv_scales fp32 [P, 64]); otherwise as mla_decode."""
+    _need(q, "q", torch.bfloat16, 4)
+    P = _fp8_cache(kv_codes, kv_scales)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, T, H, D = q.shape
+    if D != MLA_D:
+        raise ValueError("mla_decode_fp8 expects q [..., 576]")
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("batch mismatch")
+    if plan is None:
+        plan = mla_decode_plan(cache_seqlens, T, H, 1, MLA_DV)
+    if plan.shape != (B, T, H, 1, MLA_DV):
+        raise ValueError(f"plan was made for {plan.shape}")
+    if out is None:
+        out = torch.empty(B, T, H, MLA_DV, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    ws, wsb = _ws(plan)
+    _lib.check("mla_decode_fp8", _lib.lib().mla_decode_fp8(
+        _ptr(q), _ptr(kv_codes), _ptr(kv_scales), _ptr(block_table), _ptr(cache_seqlens), B, T,
+        H, P, block_table.shape[1], float(softmax_scale), int(bool(causal)),
+        _ptr(plan.sched_metadata), _ptr(plan.num_splits), ws, wsb, _ptr(out), _ptr(lse),
+        _stream()))
+    return out, lse
 
 
 def _gqla_weights(w_uk, w_uv=None):

@@ -37,6 +37,10 @@ _SIGS = {
     "gqla_absorb_query": [_P, _P, _P, _I, _I, _I, _P],
     "gqla_absorb_output": [_P, _P, _P, _I, _I, _I, _P],
     "gqla_expand_kv": [_P, _P, _P, _P, _P, ctypes.c_int64, _I, _P],
+    "mla_decode_fp8": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
+                       ctypes.c_size_t, _P, _P, _P],
+    "mla_kv_append_fp8": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
+    "mla_kv_quantize_fp8": [_P, _P, _P, ctypes.c_int64, _P],
     "mla_decode_plan_host": [_P, _I, _I, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PlanInfo)],
     "mla_status_string": [ctypes.c_int],
     "mla_profile_events": [_P, _P],

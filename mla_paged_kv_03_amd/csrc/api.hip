@@ -115,8 +115,8 @@ int check_decode_args(bool gqa, const void* q, const void* k, const void* v,
   return MLA_OK;
 }
 
-int run_decode(int B, int T, int H, int G, int DV, bool rope_k, const void* q, const void* k,
-               const void* v,
+int run_decode(int B, int T, int H, int G, int DV, int kind, const void* q, const void* k,
+               const void* v, const float* kscale,
                const int32_t* block_table, const int32_t* seqlens, int num_pages,
                int max_pages, float scale, int causal, const int32_t* meta,
                const int32_t* splits, void* ws, size_t ws_bytes, void* out, float* lse,
@@ -128,6 +128,8 @@ int run_decode(int B, int T, int H, int G, int DV, bool rope_k, const void* q, c
   if ((rc = check_decode_args(g.gqa, q, k, v, block_table, seqlens, num_pages, max_pages, scale,
                               causal, meta, splits, out, lse)) != MLA_OK)
     return rc;
+  if (kind == mla::KIND_MLA_FP8 && (!kscale || ((uintptr_t)kscale & 3)))
+    return kscale ? MLA_ERR_BAD_SHAPE : MLA_ERR_NULL_ARG;
   if ((rc = device_cus(&cus)) != MLA_OK) return rc;
   make_geom(B, T, H, G, DV, cus, &g);
   if (g.ws_bytes) {
@@ -140,6 +142,7 @@ int run_decode(int B, int T, int H, int G, int DV, bool rope_k, const void* q, c
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
+  a.kscale = kscale;
   a.block_table = block_table;
   a.seqlens = seqlens;
   a.meta = meta;
@@ -153,7 +156,6 @@ int run_decode(int B, int T, int H, int G, int DV, bool rope_k, const void* q, c
   a.scale_log2 = scale * 1.4426950408889634f;
   a.causal = causal;
   if (g_prof_start && hipEventRecord(g_prof_start, st) != hipSuccess) return MLA_ERR_HIP;
-  const int kind = !g.gqa ? mla::KIND_MLA : rope_k ? mla::KIND_GQA_ROPE : mla::KIND_GQA;
   if (mla::launch_decode_kernel(a, g.nw, kind, g.W * g.RB, st) != hipSuccess) return MLA_ERR_HIP;
   if (g_prof_stop && hipEventRecord(g_prof_stop, st) != hipSuccess) return MLA_ERR_HIP;
   if (g.max_slots > 0) {
@@ -234,7 +236,7 @@ int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
                int32_t causal, const int32_t* sched_metadata, const int32_t* num_splits,
                void* workspace, size_t workspace_bytes, void* out, float* lse,
                hipStream_t stream) {
-  return run_decode(batch, s_q, h_q, 1, MLA_DV, false, q, kv_cache, nullptr, block_table, cache_seqlens, num_pages,
+  return run_decode(batch, s_q, h_q, 1, MLA_DV, mla::KIND_MLA, q, kv_cache, nullptr, nullptr, block_table, cache_seqlens, num_pages,
                     max_pages_per_seq, softmax_scale, causal, sched_metadata, num_splits,
                     workspace, workspace_bytes, out, lse, stream);
 }
@@ -245,7 +247,7 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                int32_t max_pages_per_seq, float softmax_scale, int32_t causal,
                const int32_t* sched_metadata, const int32_t* num_splits, void* workspace,
                size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
-  return run_decode(batch, s_q, h_q, h_kv, GQA_DV, false, q, k_cache, v_cache, block_table, cache_seqlens, num_pages,
+  return run_decode(batch, s_q, h_q, h_kv, GQA_DV, mla::KIND_GQA, q, k_cache, v_cache, nullptr, block_table, cache_seqlens, num_pages,
                     max_pages_per_seq, softmax_scale, causal, sched_metadata, num_splits,
                     workspace, workspace_bytes, out, lse, stream);
 }
@@ -284,13 +286,62 @@ int gqa_kv_append(const void* new_k, const void* new_v, void* k_cache, void* v_c
                        (size_t)h_kv * GQA_D * 2, num_pages, max_pages_per_seq, stream);
 }
 
+int mla_decode_fp8(const void* q, const void* kv_codes, const float* kv_scales,
+                   const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                   int32_t s_q, int32_t h_q, int32_t num_pages, int32_t max_pages_per_seq,
+                   float softmax_scale, int32_t causal, const int32_t* sched_metadata,
+                   const int32_t* num_splits, void* workspace, size_t workspace_bytes, void* out,
+                   float* lse, hipStream_t stream) {
+  return run_decode(batch, s_q, h_q, 1, MLA_DV, mla::KIND_MLA_FP8, q, kv_codes, nullptr,
+                    kv_scales, block_table, cache_seqlens, num_pages, max_pages_per_seq,
+                    softmax_scale, causal, sched_metadata, num_splits, workspace,
+                    workspace_bytes, out, lse, stream);
+}
+
+int mla_kv_append_fp8(const void* new_kv, void* kv_codes, float* kv_scales,
+                      const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                      int32_t s_q, int32_t num_pages, int32_t max_pages_per_seq,
+                      hipStream_t stream) {
+  if (batch < 0 || s_q < 1 || num_pages < 0 || max_pages_per_seq < 0) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)batch * s_q > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (!new_kv || !kv_codes || !kv_scales || !block_table || !cache_seqlens) return MLA_ERR_NULL_ARG;
+  if (!aligned16(new_kv) || !aligned16(kv_codes) || ((uintptr_t)kv_scales & 3))
+    return MLA_ERR_BAD_SHAPE;
+  mla::QuantArgs a = {};
+  a.src = (const uint16_t*)new_kv;
+  a.codes = (uint8_t*)kv_codes;
+  a.scales = kv_scales;
+  a.block_table = block_table;
+  a.seqlens = cache_seqlens;
+  a.B = batch; a.T = s_q; a.bt_stride = max_pages_per_seq; a.num_pages = num_pages;
+  return mla::launch_quantize_fp8(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_kv_quantize_fp8(const void* kv_rows, void* kv_codes, float* kv_scales, int64_t n_rows,
+                        hipStream_t stream) {
+  if (n_rows < 0) return MLA_ERR_BAD_SHAPE;
+  if (n_rows > 0x7fffffffLL) return MLA_ERR_UNSUPPORTED;
+  if (n_rows == 0) return MLA_OK;
+  if (!kv_rows || !kv_codes || !kv_scales) return MLA_ERR_NULL_ARG;
+  if (!aligned16(kv_rows) || !aligned16(kv_codes) || ((uintptr_t)kv_scales & 3))
+    return MLA_ERR_BAD_SHAPE;
+  mla::QuantArgs a = {};
+  a.src = (const uint16_t*)kv_rows;
+  a.codes = (uint8_t*)kv_codes;
+  a.scales = kv_scales;
+  a.B = (int)n_rows; a.T = 1;
+  return mla::launch_quantize_fp8(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int gqla_decode(const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
                 int32_t s_q, int32_t h_q, int32_t h_kv, int32_t num_pages,
                 int32_t max_pages_per_seq, float softmax_scale, int32_t causal,
                 const int32_t* sched_metadata, const int32_t* num_splits, void* workspace,
                 size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
-  return run_decode(batch, s_q, h_q, h_kv, GQLA_DVG, true, q, k_cache, v_cache, block_table,
+  return run_decode(batch, s_q, h_q, h_kv, GQLA_DVG, mla::KIND_GQA_ROPE, q, k_cache, v_cache,
+                    nullptr, block_table,
                     cache_seqlens, num_pages, max_pages_per_seq, softmax_scale, causal,
                     sched_metadata, num_splits, workspace, workspace_bytes, out, lse, stream);
 }

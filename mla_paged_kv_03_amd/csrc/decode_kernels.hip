@@ -77,7 +77,9 @@ struct Layout<KIND_MLA> {
   static constexpr int TILE = 64 * K_PITCH;  // one page
   static constexpr int V_BASE = 0;
   static constexpr int DMA_PER_TILE = 72;  // 1 KiB per instruction
+  static constexpr int NBUF = 2;           // page buffers (2 x 72 KiB)
   static constexpr bool K_XOR8 = true, V_XOR8 = true;
+  static constexpr bool FP8 = false;
   static __device__ __forceinline__ int k_xor(int k) { return k & 7; }
   static __device__ __forceinline__ int v_xor(int k) { return k & 7; }
 };
@@ -91,7 +93,9 @@ struct Layout<KIND_GQA> {
   static constexpr int TILE = 2 * 64 * 256;
   static constexpr int V_BASE = 64 * 256;
   static constexpr int DMA_PER_TILE = 32;
+  static constexpr int NBUF = 2;
   static constexpr bool K_XOR8 = false, V_XOR8 = false;
+  static constexpr bool FP8 = false;
   static __device__ __forceinline__ int k_xor(int k) { return (k & 7) << 1; }
   static __device__ __forceinline__ int v_xor(int k) { return (k & 7) << 1; }
 };
@@ -108,9 +112,33 @@ struct Layout<KIND_GQA_ROPE> {
   static constexpr int TILE = 64 * 384 + 64 * 256;
   static constexpr int V_BASE = 64 * 384;
   static constexpr int DMA_PER_TILE = 40;
+  static constexpr int NBUF = 2;
   static constexpr bool K_XOR8 = true, V_XOR8 = false;
+  static constexpr bool FP8 = false;
   static __device__ __forceinline__ int k_xor(int k) { return k & 7; }
   static __device__ __forceinline__ int v_xor(int k) { return (k & 7) << 1; }
+};
+
+// FP8 latent cache: 64 rows of 576 E4M3 codes (36 chunks of 16 bytes), then
+// the page's 64 fp32 token scales. Chunk c of row k sits at chunk
+// c ^ fp8_xor(k), an XOR below 4 (inside aligned groups of 4 chunks):
+// bits 3-4 of the row spread the 16 rows of a score read (8 bytes each, rows
+// 576 bytes = 16 banks apart, so rows k and k + 4 would collide) over the
+// banks, and bit 2 separates rows k and k + 4 of a transposed V read.
+template <>
+struct Layout<KIND_MLA_FP8> {
+  static constexpr int D = 576, DV = 512;
+  static constexpr int K_PITCH = 576, V_PITCH = 576;
+  static constexpr int SCALE_OFF = 64 * 576;
+  static constexpr int TILE = SCALE_OFF + 256;
+  static constexpr int V_BASE = 0;
+  static constexpr int DMA_PER_TILE = 36 + 4;  // codes, plus one scale copy per wave
+  // half-size pages: four buffers (145 KiB) keep three pages in flight
+  static constexpr int NBUF = 4;
+  static constexpr bool K_XOR8 = true, V_XOR8 = true;
+  static constexpr bool FP8 = true;
+  static __device__ __forceinline__ int k_xor(int k) { return ((k >> 3) & 3) ^ (((k >> 2) & 1) << 1); }
+  static __device__ __forceinline__ int v_xor(int k) { return k_xor(k); }
 };
 
 // Issue one 1 KiB HBM -> LDS copy: lane l's 16 bytes at sbase + voff land at
@@ -128,6 +156,28 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* sbase, uint32_t 
                :
                : "s"(lds), "v"(voff), "s"(sbase)
                : "memory", "m0");
+}
+
+// One 256-byte HBM -> LDS copy: lane l's 4 bytes at sbase + voff land at LDS
+// byte lds + 4 * l (same wait states as dma16).
+__device__ __forceinline__ void dma4(uint32_t lds, const void* sbase, uint32_t voff) {
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2 nt"
+               :
+               : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// Two E4M3 codes (bytes 0-1, or 2-3 with HI) of w as two bf16 in one word,
+// exactly (every E4M3 value is a bf16 value). Only whole words are used:
+// the pair is never split into elements.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ bf16x8 fp8x8_bf16x8(uint32_t w0, uint32_t w1) {
+  const u32x4 u = {fp8x2_bf16x2<false>(w0), fp8x2_bf16x2<true>(w0), fp8x2_bf16x2<false>(w1),
+                   fp8x2_bf16x2<true>(w1)};
+  return __builtin_bit_cast(bf16x8, u);
 }
 
 // LDS operand reads are issued this many MFMA steps ahead of their use.
@@ -219,7 +269,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr int NDMA = LY::DMA_PER_TILE / NW;  // per wave per page
   static_assert(LY::DMA_PER_TILE % NW == 0 && NDMA < 64, "page copies split evenly");
 
-  __shared__ __attribute__((aligned(1024))) char lds[2 * LY::TILE];
+  // the page buffers, reused at the end of a range for the key-part merge
+  constexpr int MERGE_BYTES = (KS - 1) * R * (NCB * 4 + 2) * 64 * 4;
+  constexpr int NB = LY::NBUF;
+  constexpr int LDS_BYTES = NB * LY::TILE > MERGE_BYTES ? NB * LY::TILE : MERGE_BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   lds_char* const lds_p = LDS_PTR(char, lds);
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds_p;
 
@@ -275,6 +329,36 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     v_off[q] = LY::V_BASE + (ks * KW + vkey) * LY::V_PITCH +
                16 * ((2 * q + ((j16 & 3) >> 1)) ^ xv) + 8 * (j16 & 1);
 
+  // FP8 pages. The score read of block kb takes row ks*KW + krow(kb, n),
+  // 8 codes (columns 32c + 8g4 ..); the rows of the blocks are chosen so
+  // that score register i of lane group g4 in blocks 2c and 2c+1 holds the
+  // key that the transposed V read (ds_read_b64_tr_b8: lane j of group g4
+  // gets rows 8g4 .. 8g4+7 of column j) puts in MFMA slot i: krow(kb, a) =
+  // 32(kb/2) + 8(a/4) + 4(kb%2) + a%4 covers each 32 keys with two blocks. A
+  // 16-key wave keeps krow = a and uses 4 of the 8 rows a V read returns.
+  auto krow = [](int kb, int a_) {
+    return KB == 1 ? a_ : 32 * (kb >> 1) + 8 * (a_ >> 2) + 4 * (kb & 1) + (a_ & 3);
+  };
+  constexpr int KB8 = LY::FP8 ? KB : 1;
+  uint32_t k8_off[KB8][2], sc_off[KB8], v8_off[4];
+  if constexpr (LY::FP8) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int row = ks * KW + krow(kb, n);
+      const int y = LY::k_xor(row);
+#pragma unroll
+      for (int cp = 0; cp < 2; ++cp)
+        k8_off[kb][cp] = row * LY::K_PITCH + 16 * ((2 * cp + (g4 >> 1)) ^ y) + 8 * (g4 & 1);
+      sc_off[kb] = LY::SCALE_OFF + 4 * (ks * KW + krow(kb, 4 * g4));
+    }
+    // rows of a 16-key wave's V read past the page's end only feed unused slots
+    const int vrow = KW >= 32 ? ks * KW + 8 * g4 + (j16 >> 1)
+                              : min(ks * KW + 4 * g4 + (j16 >> 1), 63);
+    const int yv = LY::v_xor(vrow);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v8_off[q] = vrow * LY::V_PITCH + 16 * (q ^ yv) + 8 * (j16 & 1);
+  }
+
   for (int b = bs; b <= be; ++b) {
     const int L = uniform(a.seqlens[b]);
     const int npg = sched::seq_pages(L);
@@ -300,7 +384,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const int page = sload(uniform_ptr(bt + j));
       const int nv = uniform(min(64, L - 64 * j));
       const uint32_t dst = lds0 + buf * LY::TILE;
-      if constexpr (!GQA) {
+      if constexpr (LY::FP8) {
+        // codes: a contiguous 36 KiB block, copied like the latent page; then
+        // every wave copies the page's 64 scales to the same LDS words (the
+        // same bytes, so the waves need not agree on who does it)
+        const char* pbase = uniform_ptr((const char*)a.k + (size_t)page * LY::SCALE_OFF);
+#pragma unroll
+        for (int t = 0; t < 36 / NW; ++t) {
+          const int i = wave + NW * t;
+          const int u = 64 * i + lane;
+          const int r = u / 36, x = u - 36 * r;
+          dma16(dst + 1024 * i, pbase, min(r, nv - 1) * LY::K_PITCH + 16 * (x ^ LY::k_xor(r)));
+        }
+        const char* sbase = uniform_ptr((const char*)a.kscale + (size_t)page * 256);
+        dma4(dst + LY::SCALE_OFF, sbase, 4 * min(lane, nv - 1));
+      } else if constexpr (!GQA) {
         // the page is one contiguous 72 KiB block in HBM and in LDS: copy i
         // fills LDS bytes 1024i .. 1024i+1023, 16-byte unit u = 64i + lane,
         // i.e. chunk x of row r; rows past the sequence end repeat its last
@@ -378,14 +476,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     l = 0.f;
     bool over = false;
 
-    issue_page(p0, 0);
+    // ring of NB page buffers: NB - 1 pages in flight ahead of the one
+    // computed; page j + NB - 1 goes to the buffer page j - 1 used, which
+    // every wave left at the barrier ending iteration j - 1
+#pragma unroll
+    for (int k = 0; k < NB - 1; ++k)
+      if (p0 + k < p1) issue_page(p0 + k, k);
+    int cur = 0;
     for (int j = p0; j < p1; ++j) {
-      const int cur = (j - p0) & 1;
-      if (j + 1 < p1) {
-        issue_page(j + 1, cur ^ 1);
-        wait_vm<NDMA>();
+      if (j + NB - 1 < p1) issue_page(j + NB - 1, cur == 0 ? NB - 1 : cur - 1);
+      // this wave's copies still in flight after page j's: those of pages
+      // j+1 .. min(j + NB - 1, p1 - 1)
+      const int ahead = min(NB - 1, p1 - 1 - j);
+      if constexpr (NB == 2) {
+        if (ahead > 0) wait_vm<NDMA>(); else wait_vm<0>();
       } else {
-        wait_vm<0>();
+        static_assert(NB == 4 && 3 * NDMA < 64, "wait counts fit vmcnt");
+        if (ahead >= 3) wait_vm<3 * NDMA>();
+        else if (ahead == 2) wait_vm<2 * NDMA>();
+        else if (ahead == 1) wait_vm<NDMA>();
+        else wait_vm<0>();
       }
       barrier();
       // LDS operands are addressed as a per-lane pointer into this page's
@@ -398,6 +508,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const lds_char* vp[NVO];
 #pragma unroll
       for (int q = 0; q < NVO; ++q) vp[q] = buf + v_off[q];
+      const lds_char* kp8[KB8][2];
+      const lds_char* vp8[4];
+      if constexpr (LY::FP8) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          kp8[kb][0] = buf + k8_off[kb][0];
+          kp8[kb][1] = buf + k8_off[kb][1];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vp8[q] = buf + v8_off[q];
+      }
 
       // S^T = K . Q^T, one 16-key block per kb. Steps run d-chunk-major
       // (st = c * KB + kb) into four accumulators (st % 4), so consecutive
@@ -406,6 +527,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       // ahead of the MFMA that uses them.
       auto k_frag = [&](int st) -> bf16x8 {
         const int c = st / KB, kb = st % KB;
+        if constexpr (LY::FP8) {
+          const lds_char* p = kp8[kb][c & 1] + 64 * (c >> 1);
+          const u32x2 w = *(const __attribute__((address_space(3))) u32x2*)p;
+          return fp8x8_bf16x8(w[0], w[1]);
+        }
         const lds_char* p = LY::K_XOR8 ? kp[c & 1] + kb * 16 * LY::K_PITCH + 128 * (c >> 1)
                                        : kp[c % NQO] + kb * 16 * LY::K_PITCH;
         return *(const __attribute__((address_space(3))) bf16x8*)p;
@@ -433,15 +559,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int i = kb + KB; i < 4; i += KB) s[kb] += acc[i];
       }
 
-      // scale, mask, running max over this wave's keys
+      // scale, mask, running max over this wave's keys (FP8: times each
+      // key's token scale, which multiplies the whole K row)
       float tmax = -INFINITY;
       const int kbase = 64 * j + ks * KW;
+      f32x4 ksc[KB8];
+      if constexpr (LY::FP8) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          ksc[kb] = *(const __attribute__((address_space(3))) f32x4*)(buf + sc_off[kb]);
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = kbase + 16 * kb + 4 * g4 + i;
-          const float x = key < vis ? s[kb][i] * a.scale_log2 : -INFINITY;
+          const int key = kbase + (LY::FP8 ? krow(kb, 4 * g4) : 16 * kb + 4 * g4) + i;
+          const float sc = LY::FP8 ? a.scale_log2 * ksc[kb][i] : a.scale_log2;
+          const float x = key < vis ? s[kb][i] * sc : -INFINITY;
           s[kb][i] = x;
           tmax = fmaxf(tmax, x);
         }
@@ -473,7 +607,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = fast_exp2(s[kb][i] - m_use);
-          s[kb][i] = p;
+          // FP8: the V row is scaled by its token scale too; l is not
+          s[kb][i] = LY::FP8 ? p * ksc[kb][i] : p;
           psum += p;
         }
       l += sum4groups(psum);
@@ -498,6 +633,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         // hit different output blocks; V^T fragments are read PF steps ahead
         auto v_frag = [&](int st) -> bf16x8 {
           const int c = st / NCB, cb = st % NCB;
+          if constexpr (LY::FP8) {
+            const lds_char* p = vp8[cb & 3] + 64 * (cb >> 2) + (32 * c) * LY::V_PITCH;
+            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+            return fp8x8_bf16x8((uint32_t)w[0], (uint32_t)w[1]);
+          }
           const lds_char* p = (32 * c) * LY::V_PITCH +
                               (LY::V_XOR8 ? vp[cb & 3] + 128 * (cb >> 2) : vp[cb % NVO]);
           const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
@@ -524,6 +664,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         px[1] = pack_bf16x2(s[0][2], s[0][3]);
         const bf16x4 pf = __builtin_bit_cast(bf16x4, px);
         auto v_frag = [&](int cb) -> bf16x4 {
+          if constexpr (LY::FP8) {
+            const lds_char* p = vp8[cb & 3] + 64 * (cb >> 2);
+            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+            const u32x2 u = {fp8x2_bf16x2<false>((uint32_t)w[0]), fp8x2_bf16x2<true>((uint32_t)w[0])};
+            return __builtin_bit_cast(bf16x4, u);
+          }
           const lds_char* p = LY::V_XOR8 ? vp[cb & 3] + 128 * (cb >> 2) : vp[cb % NVO];
           return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
         };
@@ -539,6 +685,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
       }
       barrier();  // every wave is done with this buffer before it is refilled
+      cur = cur + 1 == NB ? 0 : cur + 1;
     }
     return over;
     };
@@ -550,6 +697,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     if constexpr (KS > 1) {
       float* red = (float*)lds;  // [KS-1][R][NCB*4 + 2][64] floats
       constexpr int PER = NCB * 4 + 2;
+      static_assert((KS - 1) * R * PER * 64 * 4 <= LDS_BYTES, "the merge fits in LDS");
       if (ks > 0) {
         float* my = red + ((ks - 1) * R + rg) * PER * 64 + lane;
 #pragma unroll
@@ -626,6 +774,7 @@ hipError_t launch_decode_kernel(const DecodeArgs& a, int row_groups, int kind, i
     case KIND_MLA: return launch_kind<KIND_MLA>(a, row_groups, grid, st);
     case KIND_GQA: return launch_kind<KIND_GQA>(a, row_groups, grid, st);
     case KIND_GQA_ROPE: return launch_kind<KIND_GQA_ROPE>(a, row_groups, grid, st);
+    case KIND_MLA_FP8: return launch_kind<KIND_MLA_FP8>(a, row_groups, grid, st);
   }
   return hipErrorInvalidValue;
 }

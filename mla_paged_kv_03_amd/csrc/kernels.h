@@ -11,12 +11,14 @@ enum : int {
   KIND_MLA = 0,       // latent rows of 576 (V = the first 512 columns), one KV head
   KIND_GQA = 1,       // separate 128-wide K and V rows per KV head
   KIND_GQA_ROPE = 2,  // 192-wide K rows (128 + 64 rope) and 128-wide V rows per KV head
+  KIND_MLA_FP8 = 3,   // latent rows of 576 E4M3 codes with one fp32 scale per token
 };
 
 struct DecodeArgs {
   const uint16_t* q;           // [B, T, H, D]
   const uint16_t* k;           // [P, 64, G, D]
   const uint16_t* v;           // [P, 64, G, DV]; null: V = K[..., :DV]
+  const float* kscale;         // [P, 64] per-token scales of an FP8 cache, else null
   const int32_t* block_table;  // [B, bt_stride]
   const int32_t* seqlens;      // [B]
   const int32_t* meta;         // worker records [W][REC], then unit prefix [B + 1]
@@ -80,6 +82,20 @@ struct Cols64Args {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_copy_cols64(const Cols64Args& a, hipStream_t st);
+
+// FP8 quantisation of 576-wide bf16 latent rows: row r of src (r < B * T)
+// goes to row r of dst (block_table null), or, as an append, to the slot of
+// new token t = r % T of sequence b = r / T (same rule as AppendArgs).
+struct QuantArgs {
+  const uint16_t* src;         // [B * T, 576] bf16
+  uint8_t* codes;              // [rows or P * 64, 576] E4M3
+  float* scales;               // [rows or P * 64]
+  const int32_t* block_table;  // [B, bt_stride] or null
+  const int32_t* seqlens;      // [B] (append only)
+  int B, T, bt_stride, num_pages;
+};
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t st);
 
 // Paged KV append: one wave per new token.
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t st);

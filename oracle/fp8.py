@@ -12,10 +12,12 @@ reading, listed in the design notes:
     infinities; the largest finite value is 448;
   * one float32 scale per cached token (the whole 576-wide latent row):
     value = e4m3(code) * scale;
-  * quantisation of a bf16 row x: amax = max |x|; scale = amax / 448 in
-    float32 (1 when amax = 0); code = the E4M3 value nearest to
-    clamp(x / scale, -448, 448) (float32 division), ties to the even
-    mantissa. Every decision is taken in float32, as the GPU takes it.
+  * quantisation of a bf16 row x: amax = max |x|; the scale is the
+    smallest power of two not below the float32 quotient amax / 448, at
+    least 2^-126 (1 when amax = 0) — a power-of-two (E8M0-like) scale, as
+    the OCP microscaling formats use; code = the E4M3 value nearest to
+    clamp(x / scale, -448, 448), ties to the even mantissa. x / scale is
+    exact; the quotient amax / 448 is rounded as float32 rounds it.
 Decode with such a cache is the attention definition (as in
 oracle.attention) over the dequantised rows, in float64.
 """
@@ -70,8 +72,13 @@ def quantize_rows(rows_bf16):
     operations, rounded as float32 rounds them."""
     x = bf16_to_f64(rows_bf16).astype(np.float32)            # exact
     amax = np.max(np.abs(x), axis=-1)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    y = (x / scale[..., None]).astype(np.float32)
+    r = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    # the smallest power of two >= r, from r's float32 exponent and mantissa
+    mant, ex = np.frexp(r.astype(np.float64))                # r = mant * 2^ex, mant in [0.5, 1)
+    pow2 = np.where(mant == 0.5, np.ldexp(1.0, ex - 1), np.ldexp(1.0, ex))
+    pow2 = np.maximum(pow2, 2.0 ** -126)
+    scale = np.where(amax > 0, pow2, 1.0).astype(np.float32)
+    y = (x / scale[..., None]).astype(np.float32)            # exact: a power of two
     y = np.clip(y, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     return e4m3_round(y.astype(np.float64)), scale
 

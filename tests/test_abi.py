@@ -21,7 +21,8 @@ def test_every_declared_function_is_exported(L):
     names = _lib.header_functions()
     assert {"mla_decode_plan", "mla_decode", "gqa_decode", "attn_combine", "mla_kv_append",
             "gqa_kv_append", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output",
-            "gqla_decode"} <= set(names)
+            "gqla_decode", "mla_decode_fp8", "mla_kv_append_fp8",
+            "mla_kv_quantize_fp8"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -124,6 +125,28 @@ def test_gqla_argument_checks(L):
     assert rc == -1  # no V cache
     rc = L.gqla_decode(p, p, p, p, p, 2, 1, 12, 5, 3, 4, 0.1, 0, p, p, None, 0, p, p, None)
     assert rc == -2
+
+
+def test_fp8_argument_checks(L):
+    p = ctypes.c_void_p(64)
+    args = dict(B=2, T=1, H=8, P=5, maxp=4)
+    # q, codes, scales, bt, sl, B, T, H, P, maxp, scale, causal, meta, splits, ws, wsb, out, lse
+    rc = L.mla_decode_fp8(p, p, None, p, p, 2, 1, 8, 5, 4, 0.07, 0, p, p, None, 0, p, p, None)
+    assert rc == -1                                       # no scales
+    rc = L.mla_decode_fp8(p, p, ctypes.c_void_p(66), p, p, 2, 1, 8, 5, 4, 0.07, 0, p, p, None, 0,
+                          p, p, None)
+    assert rc == -2                                       # misaligned scales
+    rc = L.mla_decode_fp8(p, p, p, p, p, 2, 0, 8, 5, 4, 0.07, 0, p, p, None, 0, p, p, None)
+    assert rc == -2
+    # new_kv, codes, scales, bt, sl, batch, s_q, num_pages, max_pages
+    assert L.mla_kv_append_fp8(p, p, p, p, p, 0, 1, 4, 4, None) == 0
+    assert L.mla_kv_append_fp8(p, p, None, p, p, 2, 1, 4, 4, None) == -1
+    assert L.mla_kv_append_fp8(p, ctypes.c_void_p(72), p, p, p, 2, 1, 4, 4, None) == -2
+    assert L.mla_kv_append_fp8(p, p, p, p, p, 2, 0, 4, 4, None) == -2
+    assert L.mla_kv_quantize_fp8(p, p, p, 0, None) == 0
+    assert L.mla_kv_quantize_fp8(None, p, p, 4, None) == -1
+    assert L.mla_kv_quantize_fp8(p, p, p, -1, None) == -2
+    assert L.mla_kv_quantize_fp8(p, p, p, 1 << 31, None) == -3
 
 
 # ------------------------------------------------------------ the schedule

@@ -63,19 +63,38 @@ def test_every_finite_value_rounds_to_its_own_code_and_ties_go_even():
 def test_quantiser_scale_rule_and_error_bound():
     d = make_inputs(CONFIGS[1])
     rows = d["kv"][:, :, 0, :].reshape(-1, 576)
+    rows = np.concatenate([rows, _special_rows()])
     codes, scales = fp8.quantize_rows(rows)
     x = oracle.bf16_to_f64(rows)
     amax = np.abs(x).max(axis=1)
-    assert np.array_equal(scales, (amax.astype(np.float32) / np.float32(448)).astype(np.float32))
-    # the largest element lands on +-448
+    live = amax > 0
+    # a power of two, the smallest one not below the float32 quotient amax / 448
+    m, _ = np.frexp(scales.astype(np.float64))
+    assert np.all(m == 0.5)
+    r = (amax.astype(np.float32) / np.float32(448)).astype(np.float64)
+    assert np.all(scales[live] >= r[live]) and np.all(scales[live] / 2 < np.maximum(r[live], 2.0 ** -125))
+    # the largest element lands in [224, 448] (225 rounds down to 224) unless
+    # the scale sits at its 2^-126 floor
     i = np.abs(x).argmax(axis=1)
-    assert np.all(np.abs(fp8.e4m3_value(codes[np.arange(len(i)), i])) == 448.0)
+    top = np.abs(fp8.e4m3_value(codes[np.arange(len(i)), i]))
+    unclamped = live & (r >= 2.0 ** -126)
+    assert unclamped.sum() < len(unclamped)  # the floor case is in the sample
+    assert scales[-1] == 2.0 ** -126           # the 1e-38 row: quotient below 2^-126
+    assert np.all((top[unclamped] >= 224) & (top[unclamped] <= 448))
     # half a step of the E4M3 grid (2^-4 relative for normals, 2^-10 absolute
-    # below 2^-6), times the scale, plus float32 rounding of x / scale
+    # below 2^-6), times the scale; x / scale itself is exact
     deq = fp8.dequantize(codes, scales)
     y = np.abs(x) / scales[:, None]
-    bound = scales[:, None] * (np.maximum(y * 2.0 ** -4, 2.0 ** -10) + y * 2.0 ** -23)
+    bound = scales[:, None] * np.maximum(y * 2.0 ** -4, 2.0 ** -10)
     assert np.all(np.abs(deq - x) <= bound)
+
+
+def _special_rows():
+    rng = np.random.default_rng(3)
+    rows = [rng.standard_normal(576) * 1e-3, rng.standard_normal(576) * 300.0,
+            np.where(np.arange(576) == 5, 1e4, 1e-2), -np.abs(rng.standard_normal(576)),
+            np.full(576, 448.0 * 2.0 ** -3), np.full(576, 1e-38)]
+    return f32_to_bf16_bits(np.stack(rows).astype(np.float32))
 
 
 def test_quantiser_zero_row_and_exact_power_of_two_rows():
