@@ -40,34 +40,54 @@ __device__ int block_scan(int v, int* wsum, int* total) {
   return r;
 }
 
+// Batches up to this many sequences keep the unit prefix and the lengths in
+// LDS, where the workers' binary searches run; larger ones search them in
+// global memory.
+constexpr int PLAN_LDS_SEQS = 8192;
+
 // One workgroup. Writes the unit prefix (B + 1 entries after the W worker
 // records), every worker record, and the exclusive prefix of partial slots
 // (B + 1 entries).
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqlens, int B, int W,
                                                            int32_t* meta, int32_t* slots) {
   __shared__ int buf[PLAN_WAVES];
+  __shared__ int32_t s_prefix[PLAN_LDS_SEQS + 1];
+  __shared__ int32_t s_len[PLAN_LDS_SEQS];
   const int tid = threadIdx.x;
   int32_t* prefix = meta + (size_t)W * sched::REC;
+  const bool in_lds = B <= PLAN_LDS_SEQS;
 
   int carry = 0, total = 0;
-  if (tid == 0) prefix[0] = 0;
+  if (tid == 0) {
+    prefix[0] = 0;
+    s_prefix[0] = 0;
+  }
   for (int base = 0; base < B; base += PLAN_THREADS) {
     const int b = base + tid;
-    const int v = b < B ? sched::seq_units(seqlens[b]) : 0;
+    const int L = b < B ? seqlens[b] : 0;
+    const int v = b < B ? sched::seq_units(L) : 0;
     const int inc = block_scan(v, buf, &total);
-    if (b < B) prefix[b + 1] = carry + inc;
+    if (b < B) {
+      prefix[b + 1] = carry + inc;
+      if (in_lds) {
+        s_prefix[b + 1] = carry + inc;
+        s_len[b] = L;
+      }
+    }
     carry += total;
   }
   __threadfence_block();
   __syncthreads();
+  const int32_t* pre = in_lds ? s_prefix : prefix;
+  const int32_t* len = in_lds ? s_len : seqlens;
 
   for (int w = tid; w < W; w += PLAN_THREADS)
-    sched::worker_record(w, W, prefix, seqlens, B, meta + (size_t)w * sched::REC);
+    sched::worker_record(w, W, pre, len, B, meta + (size_t)w * sched::REC);
 
   carry = 0;
   for (int base = 0; base < B; base += PLAN_THREADS) {
     const int b = base + tid;
-    const int v = b < B ? sched::seq_slots(b, W, prefix, seqlens, B) : 0;
+    const int v = b < B ? sched::seq_slots(b, W, pre, len, B) : 0;
     const int inc = block_scan(v, buf, &total);
     if (b < B) slots[b] = carry + inc - v;
     carry += total;
@@ -82,42 +102,103 @@ hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int32_t* met
 }
 
 // Merge the partials of one (sequence, row): lse = m + ln sum exp(lse_i - m),
-// out = sum exp(lse_i - lse) o_i. Grid (R, B); 64 threads, 4 columns each.
-__global__ __launch_bounds__(64) void combine_kernel(CombineArgs a) {
-  const int rho = blockIdx.x, b = blockIdx.y;
+// out = sum exp(lse_i - lse) o_i. One wave per row, four rows per
+// workgroup; grid (ceil(R / 4), B). Lane i holds partial i's lse (the max
+// and sum are wave reductions); lane l owns columns 4l + 256k, k < NK, and
+// reads two partial rows before summing them, so independent loads are in
+// flight together while the register count stays low enough for eight
+// waves per SIMD.
+constexpr int COMBINE_ROWS = 4;
+
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <int NK>
+__global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int rho = blockIdx.x * COMBINE_ROWS + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (rho >= a.R) return;
   const int s0 = a.slots[b];
   const int ns = a.slots[b + 1] - s0;
   if (ns <= 0) return;
   const float* pl = a.part_lse + (size_t)s0 * a.R + rho;
-  float mx = -INFINITY;
-  for (int i = 0; i < ns; ++i) mx = fmaxf(mx, pl[(size_t)i * a.R]);
+  // lane i (and i + 64, ...) holds partial i's lse
+  const float mine = lane < ns ? pl[(size_t)lane * a.R] : -INFINITY;
+  float mx = mine;
+  for (int i = lane + 64; i < ns; i += 64) mx = fmaxf(mx, pl[(size_t)i * a.R]);
+  mx = wave_max64(mx);
   uint16_t* orow = a.out + ((size_t)b * a.R + rho) * a.DV;
   if (mx == -INFINITY) {
-    for (int c = threadIdx.x * 4; c < a.DV; c += 64 * 4) *(u32x2*)(orow + c) = u32x2{0u, 0u};
-    if (threadIdx.x == 0) a.lse[(size_t)b * a.R + rho] = -INFINITY;
+    for (int c = lane * 4; c < a.DV; c += 64 * 4) *(u32x2*)(orow + c) = u32x2{0u, 0u};
+    if (lane == 0) a.lse[(size_t)b * a.R + rho] = -INFINITY;
     return;
   }
-  float tot = 0.f;
-  for (int i = 0; i < ns; ++i) tot += fast_exp2((pl[(size_t)i * a.R] - mx) * LOG2E);
+  float tot = lane < ns ? fast_exp2((mine - mx) * LOG2E) : 0.f;
+  for (int i = lane + 64; i < ns; i += 64) tot += fast_exp2((pl[(size_t)i * a.R] - mx) * LOG2E);
+  tot = wave_sum64(tot);
   const float inv = 1.f / tot;
-  for (int c = threadIdx.x * 4; c < a.DV; c += 64 * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < ns; ++i) {
-      const float wgt = fast_exp2((pl[(size_t)i * a.R] - mx) * LOG2E) * inv;
-      const f32x4 x = *(const f32x4*)(a.part_o + (((size_t)(s0 + i) * a.R + rho) * a.DV + c));
-      acc += wgt * x;
+  const float myw = lane < ns ? fast_exp2((mine - mx) * LOG2E) * inv : 0.f;
+  auto weight = [&](int i) -> float {
+    return i < 64 ? __shfl(myw, i) : fast_exp2((pl[(size_t)i * a.R] - mx) * LOG2E) * inv;
+  };
+  const float* po = a.part_o + ((size_t)s0 * a.R + rho) * a.DV;
+  const size_t pstride = (size_t)a.R * a.DV;
+  auto load = [&](int i, int k) -> f32x4 {
+    const int c = lane * 4 + 256 * k;
+    return c < a.DV ? *(const f32x4*)(po + (size_t)i * pstride + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  f32x4 acc[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int i = 0;
+  for (; i + 2 <= ns; i += 2) {
+    f32x4 x0[NK], x1[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      x0[k] = load(i, k);
+      x1[k] = load(i + 1, k);
     }
-    u32x2 y;
-    y[0] = pack_bf16x2(acc[0], acc[1]);
-    y[1] = pack_bf16x2(acc[2], acc[3]);
-    *(u32x2*)(orow + c) = y;
+    const float w0 = weight(i), w1 = weight(i + 1);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) acc[k] += w0 * x0[k] + w1 * x1[k];
   }
-  if (threadIdx.x == 0) a.lse[(size_t)b * a.R + rho] = mx + __logf(tot);
+  if (i < ns) {
+    const float w0 = weight(i);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) acc[k] += w0 * load(i, k);
+  }
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int c = lane * 4 + 256 * k;
+    if (c < a.DV) {
+      u32x2 y;
+      y[0] = pack_bf16x2(acc[k][0], acc[k][1]);
+      y[1] = pack_bf16x2(acc[k][2], acc[k][3]);
+      *(u32x2*)(orow + c) = y;
+    }
+  }
+  if (lane == 0) a.lse[(size_t)b * a.R + rho] = mx + __logf(tot);
 }
 
 hipError_t launch_combine_kernel(const CombineArgs& a, hipStream_t st) {
   if (a.B <= 0 || a.R <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(a.R, a.B), dim3(64), 0, st, a);
+  if (a.DV > 1024 || a.B > 65535) return hipErrorInvalidValue;
+  const dim3 grid((a.R + COMBINE_ROWS - 1) / COMBINE_ROWS, a.B), block(64 * COMBINE_ROWS);
+  const int nk = (a.DV + 255) / 256;
+  switch (nk) {
+    case 1: hipLaunchKernelGGL(combine_kernel<1>, grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, st, a); break;
+    default: hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, st, a); break;
+  }
   return hipGetLastError();
 }
 
