@@ -364,13 +364,8 @@ int gqla_absorb_query(const void* q, const void* w_uk, void* q_absorbed, int32_t
   a.c_outer = (int64_t)h_q * (GQLA_DC + GQLA_DR); a.c_inner = GQLA_DC + GQLA_DR;
   a.c_batch = (int64_t)hpg * (GQLA_DC + GQLA_DR);
   a.M = n_tokens * hpg; a.N = GQLA_DC; a.K = GQLA_DH; a.batches = h_kv;
-  if (mla::launch_gemm(a, stream) != hipSuccess) return MLA_ERR_HIP;
-  mla::Cols64Args r = {};
-  r.src = (const uint16_t*)q; r.dst = (uint16_t*)q_absorbed;
-  r.rows = (int64_t)n_tokens * h_q; r.reps = 1;
-  r.src_stride = GQLA_DQ; r.src_off = GQLA_DH;
-  r.dst_stride = GQLA_DC + GQLA_DR; r.dst_off = GQLA_DC;
-  return mla::launch_copy_cols64(r, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  a.rope = 1; a.rope_a_off = GQLA_DH; a.rope_c_off = GQLA_DC;  // q_rope passes through
+  return mla::launch_gemm(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int gqla_absorb_output(const void* o_latent, const void* w_uv, void* out, int32_t n_tokens,
@@ -408,24 +403,19 @@ int gqla_expand_kv(const void* kv_rows, const void* w_uk, const void* w_uv, void
   a.a_outer = GQLA_DC + GQLA_DR;
   a.b_batch = (int64_t)GQLA_DC * GQLA_DH; a.ldb = GQLA_DH; a.b_kn = 1;
   a.M = (int)n_rows; a.N = GQLA_DH; a.K = GQLA_DC; a.batches = h_kv;
-  // K: group g's columns 0..127 of each expanded row
+  // K: group g's columns 0..127 of each expanded row, plus the shared rope
   a.b = (const uint16_t*)w_uk;
   a.c = (uint16_t*)k_rows;
   a.c_outer = (int64_t)h_kv * GQLA_DQ; a.c_batch = GQLA_DQ;
+  a.rope = 1; a.rope_a_off = GQLA_DC; a.rope_c_off = GQLA_DH;
   if (mla::launch_gemm(a, stream) != hipSuccess) return MLA_ERR_HIP;
   // V
   a.b = (const uint16_t*)w_uv;
   a.b_batch = (int64_t)GQLA_DC * GQLA_DVG; a.ldb = GQLA_DVG; a.N = GQLA_DVG;
   a.c = (uint16_t*)v_rows;
   a.c_outer = (int64_t)h_kv * GQLA_DVG; a.c_batch = GQLA_DVG;
-  if (mla::launch_gemm(a, stream) != hipSuccess) return MLA_ERR_HIP;
-  // the shared rope columns into every group's K row
-  mla::Cols64Args r = {};
-  r.src = (const uint16_t*)kv_rows; r.dst = (uint16_t*)k_rows;
-  r.rows = n_rows; r.reps = h_kv;
-  r.src_stride = GQLA_DC + GQLA_DR; r.src_off = GQLA_DC;
-  r.dst_stride = GQLA_DQ; r.dst_off = GQLA_DH;
-  return mla::launch_copy_cols64(r, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  a.rope = 0;
+  return mla::launch_gemm(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q, int32_t h_q,

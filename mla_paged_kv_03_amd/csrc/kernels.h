@@ -60,7 +60,9 @@ struct AppendArgs {
 // at  base + z * batch + (m / inner) * outer + (m % inner) * inner_stride
 // (elements); rows hold K (A) or N (C) contiguous elements. B of problem z
 // starts at b + z * b_batch and is [N][ldb] with K contiguous (b_kn = 0) or
-// [K][ldb] with N contiguous (b_kn = 1). N % 128 == 0, K % 64 == 0.
+// [K][ldb] with N contiguous (b_kn = 1). N % 128 == 0, K % 64 == 0. With
+// rope set, each C row also gets 64 elements copied from its A row:
+// C[row][rope_c_off + e] = A[row][rope_a_off + e], e < 64.
 struct GemmArgs {
   const uint16_t* a;
   const uint16_t* b;
@@ -69,19 +71,10 @@ struct GemmArgs {
   int64_t b_batch;
   int64_t c_outer, c_inner, c_batch;
   int ldb, inner, M, N, K, batches, b_kn;
-};
-
-// dst[(r * reps + j) * dst_stride + dst_off + e] = src[r * src_stride + src_off + e]
-// for r < rows, j < reps, e < 64 (bf16 elements, 16-byte aligned runs).
-struct Cols64Args {
-  const uint16_t* src;
-  uint16_t* dst;
-  int64_t rows, src_stride, dst_stride;
-  int reps, src_off, dst_off;
+  int rope, rope_a_off, rope_c_off;
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
-hipError_t launch_copy_cols64(const Cols64Args& a, hipStream_t st);
 
 // FP8 quantisation of 576-wide bf16 latent rows: row r of src (r < B * T)
 // goes to row r of dst (block_table null), or, as an append, to the slot of
