@@ -260,19 +260,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   constexpr bool GQA = KIND != KIND_MLA;
   constexpr int NW = 4;
   constexpr int KS = NW / R;      // waves sharing a row group (key split)
-  constexpr int KW = 64 / KS;     // keys per wave per page
-  constexpr int KB = KW / 16;     // 16-key score blocks per wave per page
+  // FP8 pages are half the size: with one row group, a loop step takes two
+  // consecutive pages (a 128-key tile), so that each wave owns 32 keys of
+  // one page and the per-step barriers and softmax cover twice the keys.
+  constexpr int PPT = (LY::FP8 && R == 1) ? 2 : 1;  // pages per loop step
+  constexpr int KW = 64 * PPT / KS;  // keys per wave per step
+  constexpr int KB = KW / 16;        // 16-key score blocks per wave per step
+  static_assert(!LY::FP8 || KW >= 32, "FP8 waves own at least 32 keys");
   constexpr int D = LY::D, DV = LY::DV;
   constexpr int KC = D / 32;      // MFMA K steps of the score product
   constexpr int NCB = DV / 16;    // 16-wide column blocks of the output
   constexpr int ROWS = 16 * R;
-  constexpr int NDMA = LY::DMA_PER_TILE / NW;  // per wave per page
+  constexpr int NDMA = PPT * LY::DMA_PER_TILE / NW;  // per wave per step
   static_assert(LY::DMA_PER_TILE % NW == 0 && NDMA < 64, "page copies split evenly");
 
   // the page buffers, reused at the end of a range for the key-part merge
   constexpr int MERGE_BYTES = (KS - 1) * R * (NCB * 4 + 2) * 64 * 4;
-  constexpr int NB = LY::NBUF;
-  constexpr int LDS_BYTES = NB * LY::TILE > MERGE_BYTES ? NB * LY::TILE : MERGE_BYTES;
+  constexpr int NB = PPT == 2 ? 2 : LY::NBUF;  // buffers of PPT pages each
+  constexpr int STEP_BYTES = PPT * LY::TILE;
+  constexpr int LDS_BYTES = NB * STEP_BYTES > MERGE_BYTES ? NB * STEP_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   lds_char* const lds_p = LDS_PTR(char, lds);
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds_p;
@@ -329,34 +335,36 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     v_off[q] = LY::V_BASE + (ks * KW + vkey) * LY::V_PITCH +
                16 * ((2 * q + ((j16 & 3) >> 1)) ^ xv) + 8 * (j16 & 1);
 
-  // FP8 pages. The score read of block kb takes row ks*KW + krow(kb, n),
-  // 8 codes (columns 32c + 8g4 ..); the rows of the blocks are chosen so
-  // that score register i of lane group g4 in blocks 2c and 2c+1 holds the
-  // key that the transposed V read (ds_read_b64_tr_b8: lane j of group g4
-  // gets rows 8g4 .. 8g4+7 of column j) puts in MFMA slot i: krow(kb, a) =
-  // 32(kb/2) + 8(a/4) + 4(kb%2) + a%4 covers each 32 keys with two blocks. A
-  // 16-key wave keeps krow = a and uses 4 of the 8 rows a V read returns.
+  // FP8 pages. The score read of block kb takes row krow(kb, n) of the
+  // wave's keys, 8 codes (columns 32c + 8g4 ..); the rows of the blocks are
+  // chosen so that score register i of lane group g4 in blocks 2c and 2c+1
+  // holds the key that the transposed V read (ds_read_b64_tr_b8: lane j of
+  // group g4 gets rows 8g4 .. 8g4+7 of column j) puts in MFMA slot i:
+  // krow(kb, a) = 32(kb/2) + 8(a/4) + 4(kb%2) + a%4 covers each 32 keys with
+  // two blocks.
   auto krow = [](int kb, int a_) {
-    return KB == 1 ? a_ : 32 * (kb >> 1) + 8 * (a_ >> 2) + 4 * (kb & 1) + (a_ & 3);
+    return 32 * (kb >> 1) + 8 * (a_ >> 2) + 4 * (kb & 1) + (a_ & 3);
   };
   constexpr int KB8 = LY::FP8 ? KB : 1;
   uint32_t k8_off[KB8][2], sc_off[KB8], v8_off[4];
   if constexpr (LY::FP8) {
+    // this wave's keys lie in page slot ps of the step, from row r0 on
+    const uint32_t ps = (uint32_t)((ks * KW) >> 6) * LY::TILE;
+    const int r0 = (ks * KW) & 63;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int row = ks * KW + krow(kb, n);
+      const int row = r0 + krow(kb, n);
       const int y = LY::k_xor(row);
 #pragma unroll
       for (int cp = 0; cp < 2; ++cp)
-        k8_off[kb][cp] = row * LY::K_PITCH + 16 * ((2 * cp + (g4 >> 1)) ^ y) + 8 * (g4 & 1);
-      sc_off[kb] = LY::SCALE_OFF + 4 * (ks * KW + krow(kb, 4 * g4));
+        k8_off[kb][cp] = ps + row * LY::K_PITCH + 16 * ((2 * cp + (g4 >> 1)) ^ y) + 8 * (g4 & 1);
+      sc_off[kb] = ps + LY::SCALE_OFF + 4 * (r0 + krow(kb, 4 * g4));
     }
-    // rows of a 16-key wave's V read past the page's end only feed unused slots
-    const int vrow = KW >= 32 ? ks * KW + 8 * g4 + (j16 >> 1)
-                              : min(ks * KW + 4 * g4 + (j16 >> 1), 63);
+    const int vrow = r0 + 8 * g4 + (j16 >> 1);
     const int yv = LY::v_xor(vrow);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v8_off[q] = vrow * LY::V_PITCH + 16 * (q ^ yv) + 8 * (j16 & 1);
+    for (int q = 0; q < 4; ++q)
+      v8_off[q] = ps + vrow * LY::V_PITCH + 16 * (q ^ yv) + 8 * (j16 & 1);
   }
 
   for (int b = bs; b <= be; ++b) {
@@ -379,11 +387,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int split = b == bs ? rec[sched::R_SPLIT0] : 0;
     const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
 
-    // copy page j of sequence b into buffer `buf`
-    auto issue_page = [&](int j, int buf) {
+    // copy page j of sequence b to LDS byte dst
+    auto issue_page = [&](int j, uint32_t dst) {
       const int page = sload(uniform_ptr(bt + j));
       const int nv = uniform(min(64, L - 64 * j));
-      const uint32_t dst = lds0 + buf * LY::TILE;
       if constexpr (LY::FP8) {
         // codes: a contiguous 36 KiB block, copied like the latent page; then
         // every wave copies the page's 64 scales to the same LDS words (the
@@ -476,18 +483,26 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     l = 0.f;
     bool over = false;
 
-    // ring of NB page buffers: NB - 1 pages in flight ahead of the one
-    // computed; page j + NB - 1 goes to the buffer page j - 1 used, which
-    // every wave left at the barrier ending iteration j - 1
+    // a step's PPT pages from page j into buffer buf; past the worker's
+    // range the slot gets page j again (finite data whose keys are masked),
+    // so every wave issues the same number of copies per step
+    auto issue_step = [&](int j, int buf) {
+#pragma unroll
+      for (int pp = 0; pp < PPT; ++pp)
+        issue_page(j + pp < p1 ? j + pp : j, lds0 + buf * STEP_BYTES + pp * LY::TILE);
+    };
+    // ring of NB step buffers: NB - 1 steps in flight ahead of the one
+    // computed; step j + (NB - 1) PPT goes to the buffer step j - PPT used,
+    // which every wave left at the barrier ending that step
 #pragma unroll
     for (int k = 0; k < NB - 1; ++k)
-      if (p0 + k < p1) issue_page(p0 + k, k);
+      if (p0 + k * PPT < p1) issue_step(p0 + k * PPT, k);
     int cur = 0;
-    for (int j = p0; j < p1; ++j) {
-      if (j + NB - 1 < p1) issue_page(j + NB - 1, cur == 0 ? NB - 1 : cur - 1);
-      // this wave's copies still in flight after page j's: those of pages
-      // j+1 .. min(j + NB - 1, p1 - 1)
-      const int ahead = min(NB - 1, p1 - 1 - j);
+    for (int j = p0; j < p1; j += PPT) {
+      if (j + (NB - 1) * PPT < p1) issue_step(j + (NB - 1) * PPT, cur == 0 ? NB - 1 : cur - 1);
+      // this wave's copies still in flight after step j's: those of the
+      // steps issued after it, at most NB - 1
+      const int ahead = min(NB - 1, (p1 - 1 - j) / PPT);
       if constexpr (NB == 2) {
         if (ahead > 0) wait_vm<NDMA>(); else wait_vm<0>();
       } else {
@@ -501,7 +516,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       // LDS operands are addressed as a per-lane pointer into this page's
       // buffer plus a compile-time byte offset, which the compiler folds
       // into the offset field of the LDS read.
-      lds_char* const buf = lds_p + cur * LY::TILE;
+      lds_char* const buf = lds_p + cur * STEP_BYTES;
       const lds_char* kp[NQO];
 #pragma unroll
       for (int q = 0; q < NQO; ++q) kp[q] = buf + qk_off[q];
@@ -563,6 +578,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       // key's token scale, which multiplies the whole K row)
       float tmax = -INFINITY;
       const int kbase = 64 * j + ks * KW;
+      // a wave's keys lie in one page, which must be inside the worker's range
+      const bool page_ok = PPT == 1 || j + ((ks * KW) >> 6) < p1;
       f32x4 ksc[KB8];
       if constexpr (LY::FP8) {
 #pragma unroll
@@ -575,7 +592,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int key = kbase + (LY::FP8 ? krow(kb, 4 * g4) : 16 * kb + 4 * g4) + i;
           const float sc = LY::FP8 ? a.scale_log2 * ksc[kb][i] : a.scale_log2;
-          const float x = key < vis ? s[kb][i] * sc : -INFINITY;
+          const float x = (page_ok && key < vis) ? s[kb][i] * sc : -INFINITY;
           s[kb][i] = x;
           tmax = fmaxf(tmax, x);
         }
@@ -664,12 +681,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         px[1] = pack_bf16x2(s[0][2], s[0][3]);
         const bf16x4 pf = __builtin_bit_cast(bf16x4, px);
         auto v_frag = [&](int cb) -> bf16x4 {
-          if constexpr (LY::FP8) {
-            const lds_char* p = vp8[cb & 3] + 64 * (cb >> 2);
-            const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
-            const u32x2 u = {fp8x2_bf16x2<false>((uint32_t)w[0]), fp8x2_bf16x2<true>((uint32_t)w[0])};
-            return __builtin_bit_cast(bf16x4, u);
-          }
           const lds_char* p = LY::V_XOR8 ? vp[cb & 3] + 128 * (cb >> 2) : vp[cb % NVO];
           return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
         };
