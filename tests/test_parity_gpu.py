@@ -245,7 +245,7 @@ def _climbing_scores(d, cfg, period=5, step=18.0, seed=7):
 
 
 @pytest.mark.parametrize("period", [3, 5])
-@pytest.mark.parametrize("kind", ["mla", "gqa"])
+@pytest.mark.parametrize("kind", ["mla", "mla_h128", "gqa"])
 def test_scores_climbing_from_page_to_page(dev, kind, period):
     """Scores rise by 18 (log2 units) from page to page within runs of
     `period` pages, far more than the rescale slack. With period 3 a row's
@@ -256,7 +256,10 @@ def test_scores_climbing_from_page_to_page(dev, kind, period):
     consecutive pages (the batch has far more pages than workers)."""
     import mla_paged_kv_03_amd as lib
     Ls = (64 * 300, 64 * 280 + 17, 64 * 300, 64 * 290)
-    cfg = (_mla(4, 1, 16, Ls, False) if kind == "mla" else _gqa(4, 1, 16, 2, Ls))
+    # 128 heads: the 128-row workgroups, whose fallback is a max-only pass
+    cfg = {"mla": lambda: _mla(4, 1, 16, Ls, False),
+           "mla_h128": lambda: _mla(4, 1, 128, Ls, False),
+           "gqa": lambda: _gqa(4, 1, 16, 2, Ls)}[kind]()
     d = inputs(cfg, seed=12)
     _climbing_scores(d, cfg, period=period)
     t = to_device(d, dev)
