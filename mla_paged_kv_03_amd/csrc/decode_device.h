@@ -25,6 +25,12 @@ __device__ __forceinline__ void decode_block_id(int bid, int W, int RB, int& w, 
   }
 }
 
+// Waves per decode workgroup: four compute waves, plus four copy waves for
+// the bf16 latent cache at 64 query rows per workgroup, where every page is
+// copied once per row block and the copies cost the compute waves as much
+// time as the products when they issue them themselves.
+constexpr int decode_waves(int R, int KIND) { return (KIND == KIND_MLA && R == 4) ? 8 : 4; }
+
 // LDS page layouts (bytes). Row k of a page keeps its 16-byte chunk c at
 // k * PITCH + 16 * (c ^ xor(k)). Measured on gfx950 (whose LDS serves 256
 // bytes per clock), these choices let the K-operand reads (16 rows x 16 bytes

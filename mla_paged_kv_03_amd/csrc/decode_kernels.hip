@@ -39,10 +39,19 @@
 namespace mla {
 
 template <int R, int KIND>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(DecodeArgs a) {
   using LY = Layout<KIND>;
   constexpr bool GQA = KIND != KIND_MLA;
-  constexpr int NW = 4;
+  constexpr int NW = 4;           // compute waves
+  // With copy waves, waves NW .. 2NW-1 issue every page copy and compute
+  // nothing, so the compute waves never stall behind the address unit.
+  constexpr bool PROD = decode_waves(R, KIND) > NW;
+  constexpr int NWT = decode_waves(R, KIND);
+  static_assert(!PROD || (R == 4 && !LY::FP8 && !GQA), "copy waves: latent bf16, 64 rows");
+  // LDS operand prefetch distance; two waves per SIMD leave 256 registers a
+  // wave, which hold O (128), Q (72) and two steps of operands (also the
+  // fastest distance measured for this kernel: 2 < 1 < 3, 4, 6)
+  constexpr int PFD = PROD ? 2 : PF;
   constexpr int KS = NW / R;      // waves sharing a row group (key split)
   // FP8 pages are half the size: with one row group, a loop step takes two
   // consecutive pages (a 128-key tile), so that each wave owns 32 keys of
@@ -69,6 +78,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
+  const bool producer = PROD && wave >= NW;
+  const int cw = PROD ? wave - NW : wave;  // index among the copying waves
   const int lane = tid & 63;
   const int n = lane & 15;     // query row within the wave's 16
   const int g4 = lane >> 4;    // 16-lane group
@@ -87,7 +98,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
   const int hpg = a.H / a.G;
   const int r = rblk * ROWS + rg * 16 + n;  // row within this KV head
-  const bool row_ok = r < a.M;
+  const bool row_ok = !producer && r < a.M;
   const int t = row_ok ? r / hpg : 0;
   const int h = g * hpg + (row_ok ? r - t * hpg : 0);
   const int rho = t * a.H + h;               // output row within a sequence
@@ -151,6 +162,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       v8_off[q] = ps + vrow * LY::V_PITCH + 16 * (q ^ yv) + 8 * (j16 & 1);
   }
 
+  // The sequences of the worker's range. With copy waves the two roles run
+  // separate instances of this loop (CW: a copy wave), meeting at the same
+  // barriers, so that neither keeps the other's registers live.
+  auto seq_loop = [&](auto copy_role) {
+  constexpr bool CW = decltype(copy_role)::value;
   for (int b = bs; b <= be; ++b) {
     const int L = uniform(a.seqlens[b]);
     const int npg = sched::seq_pages(L);
@@ -160,7 +176,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int nslots = uniform(a.slots[b + 1]) - s0;
 
     if (npg == 0) {
-      if ((b > bs || rec[sched::R_OWNS_FIRST]) && row_ok && ks == 0) {
+      if (!CW && (b > bs || rec[sched::R_OWNS_FIRST]) && row_ok && ks == 0) {
         uint16_t* o = a.out + ((size_t)b * TH + rho) * DV;
         for (int cb = 0; cb < NCB; ++cb) *(u32x2*)(o + 16 * cb + 4 * g4) = u32x2{0u, 0u};
         if (g4 == 0) a.lse[(size_t)b * TH + rho] = -INFINITY;
@@ -182,7 +198,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const char* pbase = uniform_ptr((const char*)a.k + (size_t)page * LY::SCALE_OFF);
 #pragma unroll
         for (int t = 0; t < 36 / NW; ++t) {
-          const int i = wave + NW * t;
+          const int i = cw + NW * t;
           const int u = 64 * i + lane;
           const int r = u / 36, x = u - 36 * r;
           dma16(dst + 1024 * i, pbase, min(r, nv - 1) * LY::K_PITCH + 16 * (x ^ LY::k_xor(r)));
@@ -197,7 +213,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const char* pbase = uniform_ptr((const char*)a.k + (size_t)page * LY::TILE);
 #pragma unroll
         for (int t = 0; t < LY::DMA_PER_TILE / NW; ++t) {
-          const int i = wave + NW * t;
+          const int i = cw + NW * t;
           const int u = 64 * i + lane;
           const int r = u / 72, x = u - 72 * r;
           const uint32_t vo = min(r, nv - 1) * LY::K_PITCH + 16 * (x ^ LY::k_xor(r));
@@ -216,14 +232,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         const char* vbase = uniform_ptr((const char*)a.v + row0 * (LY::DV * 2));
 #pragma unroll
         for (int t = 0; t < KC16 / NW; ++t) {
-          const int i = wave + NW * t;
+          const int i = cw + NW * t;
           const int u = 64 * i + lane;
           const int r = u / KC16, x = u - KC16 * r;
           dma16(dst + 1024 * i, kbase, min(r, nv - 1) * kstride + 16 * (x ^ LY::k_xor(r)));
         }
 #pragma unroll
         for (int t = 0; t < VC16 / NW; ++t) {
-          const int i = wave + NW * t;
+          const int i = cw + NW * t;
           const int u = 64 * i + lane;
           const int r = u / VC16, x = u - VC16 * r;
           dma16(dst + LY::V_BASE + 1024 * i, vbase,
@@ -234,7 +250,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     // queries of this lane's row, as B operands of the score MFMA
     bf16x8 qf[KC];
-    {
+    if constexpr (!CW) {
       const uint16_t* qrow = a.q + ((size_t)b * TH + rho) * D;
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
@@ -275,28 +291,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       for (int pp = 0; pp < PPT; ++pp)
         issue_page(j + pp < p1 ? j + pp : j, lds0 + buf * STEP_BYTES + pp * LY::TILE);
     };
-    // ring of NB step buffers: NB - 1 steps in flight ahead of the one
-    // computed; step j + (NB - 1) PPT goes to the buffer step j - PPT used,
-    // which every wave left at the barrier ending that step
-#pragma unroll
-    for (int k = 0; k < NB - 1; ++k)
-      if (p0 + k * PPT < p1) issue_step(p0 + k * PPT, k);
-    int cur = 0;
-    for (int j = p0; j < p1; j += PPT) {
-      if (j + (NB - 1) * PPT < p1) issue_step(j + (NB - 1) * PPT, cur == 0 ? NB - 1 : cur - 1);
-      // this wave's copies still in flight after step j's: those of the
-      // steps issued after it, at most NB - 1
-      const int ahead = min(NB - 1, (p1 - 1 - j) / PPT);
-      if constexpr (NB == 2) {
-        if (ahead > 0) wait_vm<NDMA>(); else wait_vm<0>();
-      } else {
-        static_assert(NB == 4 && 3 * NDMA < 64, "wait counts fit vmcnt");
-        if (ahead >= 3) wait_vm<3 * NDMA>();
-        else if (ahead == 2) wait_vm<2 * NDMA>();
-        else if (ahead == 1) wait_vm<NDMA>();
-        else wait_vm<0>();
-      }
-      barrier();
+    // step j's scores, softmax update and P V from step buffer cur
+    auto compute_step = [&](int j, int cur) {
       // LDS operands are addressed as a per-lane pointer into this page's
       // buffer plus a compile-time byte offset, which the compiler folds
       // into the offset field of the LDS read.
@@ -322,7 +318,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       // S^T = K . Q^T, one 16-key block per kb. Steps run d-chunk-major
       // (st = c * KB + kb) into four accumulators (st % 4), so consecutive
       // MFMAs never depend on each other; blocks that own several
-      // accumulators sum them afterwards. K fragments are read PF steps
+      // accumulators sum them afterwards. K fragments are read PFD steps
       // ahead of the MFMA that uses them.
       auto k_frag = [&](int st) -> bf16x8 {
         const int c = st / KB, kb = st % KB;
@@ -336,7 +332,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         return *(const __attribute__((address_space(3))) bf16x8*)p;
       };
       constexpr int NQK = KB * KC;
-      constexpr int PFK = NQK < PF ? NQK : PF;
+      constexpr int PFK = NQK < PFD ? NQK : PFD;
       static_assert(KB <= 4 && 4 % KB == 0, "score blocks map onto four accumulators");
       f32x4 acc[4];
 #pragma unroll
@@ -431,7 +427,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           pf[c] = __builtin_bit_cast(bf16x8, x);
         }
         // steps run key-chunk-major (st = c * NCB + cb): consecutive MFMAs
-        // hit different output blocks; V^T fragments are read PF steps ahead
+        // hit different output blocks; V^T fragments are read PFD steps ahead
         auto v_frag = [&](int st) -> bf16x8 {
           const int c = st / NCB, cb = st % NCB;
           if constexpr (LY::FP8) {
@@ -447,7 +443,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         };
         constexpr int NST = NCB * PC;
-        constexpr int PFV = NST < PF ? NST : PF;
+        constexpr int PFV = NST < PFD ? NST : PFD;
         bf16x8 vf[PFV + 1];
 #pragma unroll
         for (int st = 0; st < PFV; ++st) vf[st] = v_frag(st);
@@ -468,7 +464,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           const lds_char* p = LY::V_XOR8 ? vp[cb & 3] + 128 * (cb >> 2) : vp[cb % NVO];
           return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
         };
-        constexpr int PFV = NCB < PF ? NCB : PF;
+        constexpr int PFV = NCB < PFD ? NCB : PFD;
         bf16x4 vf[PFV + 1];
 #pragma unroll
         for (int cb = 0; cb < PFV; ++cb) vf[cb] = v_frag(cb);
@@ -479,13 +475,63 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           mem_fence_compiler();
         }
       }
-      barrier();  // every wave is done with this buffer before it is refilled
-      cur = cur + 1 == NB ? 0 : cur + 1;
+    };
+
+    if constexpr (PROD) {
+      // The copy waves fill one buffer while the compute waves read the
+      // other. At the barrier opening step j, step j's copies have landed
+      // (each copy wave waited for its own) and step j - 1's compute is
+      // done, so step j + 1 may refill that buffer.
+      if constexpr (CW) {
+        if (p0 < p1) issue_step(p0, 0);
+        int cur = 0;
+        for (int j = p0; j < p1; ++j) {
+          wait_vm<0>();
+          barrier();
+          if (j + 1 < p1) issue_step(j + 1, cur ^ 1);
+          cur ^= 1;
+        }
+      } else {
+        int cur = 0;
+        for (int j = p0; j < p1; ++j) {
+          barrier();
+          compute_step(j, cur);
+          cur ^= 1;
+        }
+      }
+      barrier();  // the last buffer is read before anything refills it
+    } else {
+      // ring of NB step buffers: NB - 1 steps in flight ahead of the one
+      // computed; step j + (NB - 1) PPT goes to the buffer step j - PPT used,
+      // which every wave left at the barrier ending that step
+#pragma unroll
+      for (int k = 0; k < NB - 1; ++k)
+        if (p0 + k * PPT < p1) issue_step(p0 + k * PPT, k);
+      int cur = 0;
+      for (int j = p0; j < p1; j += PPT) {
+        if (j + (NB - 1) * PPT < p1) issue_step(j + (NB - 1) * PPT, cur == 0 ? NB - 1 : cur - 1);
+        // this wave's copies still in flight after step j's: those of the
+        // steps issued after it, at most NB - 1
+        const int ahead = min(NB - 1, (p1 - 1 - j) / PPT);
+        if constexpr (NB == 2) {
+          if (ahead > 0) wait_vm<NDMA>(); else wait_vm<0>();
+        } else {
+          static_assert(NB == 4 && 3 * NDMA < 64, "wait counts fit vmcnt");
+          if (ahead >= 3) wait_vm<3 * NDMA>();
+          else if (ahead == 2) wait_vm<2 * NDMA>();
+          else if (ahead == 1) wait_vm<NDMA>();
+          else wait_vm<0>();
+        }
+        barrier();
+        compute_step(j, cur);
+        barrier();  // every wave is done with this buffer before it is refilled
+        cur = cur + 1 == NB ? 0 : cur + 1;
+      }
     }
     return over;
     };
     // every wave runs the same passes: the page buffers and barriers are shared
-    if (block_or<NW>(run_range(std::true_type{}), lds_p, wave)) run_range(std::false_type{});
+    if (block_or<NWT>(run_range(std::true_type{}), lds_p, wave)) run_range(std::false_type{});
 
     // merge the key parts of each row group through LDS (page buffers are
     // free: every copy has landed and every wave has passed the last barrier)
@@ -523,7 +569,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
 
     // epilogue: normalise; lane l holds dv = 16cb + 4(l/16) + i
-    if (row_ok && ks == 0) {
+    if (!CW && row_ok && ks == 0) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const float lse_v = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
     if (nslots == 0) {
@@ -545,11 +591,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
     }
   }
+  };
+  if constexpr (PROD) {
+    if (producer) seq_loop(std::true_type{});
+    else seq_loop(std::false_type{});
+  } else {
+    seq_loop(std::false_type{});
+  }
 }
 
 template <int R, int KIND>
 static hipError_t launch_decode(const DecodeArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<R, KIND>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_kernel<R, KIND>), dim3(grid), dim3(64 * decode_waves(R, KIND)), 0,
+                     st, a);
   return hipGetLastError();
 }
 
