@@ -220,13 +220,26 @@ __device__ __forceinline__ bool block_or(bool x, lds_char* lds_p, int wave) {
   return r != 0;
 }
 
+// Reductions over the four 16-lane groups (lanes l, l ^ 16, l ^ 32,
+// l ^ 48) with gfx950's lane swaps, which stay in the VALU: swapping the odd
+// 16-lane rows of one copy of x with the even rows of another leaves
+// {x[l], x[l ^ 16]} in the two results of lane l (the 32-lane swap likewise
+// {x[l], x[l ^ 32]}), and the pair's max or sum is the same in both lanes.
 __device__ __forceinline__ float max4groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  uint32_t u = __float_as_uint(x);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  u = __float_as_uint(x);
+  p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float sum4groups(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  uint32_t u = __float_as_uint(x);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  u = __float_as_uint(x);
+  p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 }  // namespace mla
