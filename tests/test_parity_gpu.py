@@ -256,7 +256,7 @@ def test_scores_climbing_from_page_to_page(dev, kind, period):
     consecutive pages (the batch has far more pages than workers)."""
     import mla_paged_kv_03_amd as lib
     Ls = (64 * 300, 64 * 280 + 17, 64 * 300, 64 * 290)
-    # 128 heads: the 128-row workgroups, whose fallback is a max-only pass
+    # 128 heads: the 64-row workgroups whose page copies come from copy waves
     cfg = {"mla": lambda: _mla(4, 1, 16, Ls, False),
            "mla_h128": lambda: _mla(4, 1, 128, Ls, False),
            "gqa": lambda: _gqa(4, 1, 16, 2, Ls)}[kind]()
