@@ -324,6 +324,27 @@ int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q
                          int32_t* sched_metadata_host, int32_t* num_splits_host,
                          mla_plan_info* info);
 
+/* Debug check of the device-side preconditions above, for callers that
+ * want to validate a block table and lengths before a decode call (an
+ * out-of-range page there is an out-of-bounds read). One small kernel on
+ * `stream` reads cache_seqlens[0 .. batch) and, for each sequence whose
+ * length is valid, block_table[b, j] for j < ceil(L_b / 64) (row stride
+ * max_pages_per_seq), and writes status (device, int32 [4], 4-byte aligned,
+ * no initialisation needed):
+ *   status[0] = number of violations: lengths outside [0, 64 * max_pages_per_seq]
+ *               plus used entries outside [0, num_pages);
+ *   status[1] = sequence of the first violation in (b, j) order, or -1;
+ *   status[2] = its page index j, or -1 when the length itself is invalid
+ *               (0 when there is no violation);
+ *   status[3] = the offending value (the length or the page id), else 0.
+ * Pages of a sequence with an invalid length are not checked.
+ * Errors: MLA_ERR_NULL_ARG for status = NULL, or a NULL table when batch > 0;
+ * MLA_ERR_BAD_SHAPE for batch < 0, num_pages < 1, max_pages_per_seq < 1 or a
+ * misaligned status. */
+int mla_check_pages(const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                    int32_t num_pages, int32_t max_pages_per_seq, int32_t* status,
+                    hipStream_t stream);
+
 /* Profiling hook: while set, every mla_decode / gqa_decode call records the
  * HIP event `start` on its stream right before its main decode kernel and
  * `stop` right after it (before any merge kernel), so a caller can time that

@@ -22,7 +22,7 @@ from ._lib import DecodeError, PlanInfo
 __all__ = ["Plan", "PlanInfo", "DecodeError", "plan_info", "mla_decode_plan", "mla_decode",
            "gqa_decode", "attn_combine", "mla_kv_append", "gqa_kv_append",
            "mla_decode_fp8", "mla_kv_append_fp8", "mla_kv_quantize_fp8", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output", "gqla_decode",
-           "mla_decode_plan_host", "profile_events"]
+           "mla_decode_plan_host", "mla_check_pages", "profile_events"]
 
 MLA_D, MLA_DV = 576, 512
 GQA_D = 128
@@ -407,6 +407,25 @@ def attn_combine(o_partial, lse_partial, num_splits, out=None, lse=None):
         _ptr(o_partial), _ptr(lse_partial), _ptr(num_splits), B, R, dv, _ptr(out), _ptr(lse),
         _stream()))
     return out, lse
+
+
+def mla_check_pages(block_table, cache_seqlens, num_pages, status=None):
+    """Check the decode calls' device-side preconditions: every length in
+    [0, 64 * max_pages] and every used block-table entry in [0, num_pages).
+    block_table int32 [B, max_pages], cache_seqlens int32 [B]. Returns status
+    int32 [4] on the device, filled asynchronously: [violations, first
+    sequence or -1, its page index (-1: the length), offending value]."""
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, max_pages = block_table.shape
+    if cache_seqlens.shape[0] != B:
+        raise ValueError("cache_seqlens must have one entry per block-table row")
+    if status is None:
+        status = torch.empty(4, dtype=torch.int32, device=block_table.device)
+    _lib.check("mla_check_pages", _lib.lib().mla_check_pages(
+        _ptr(block_table), _ptr(cache_seqlens), B, int(num_pages), max_pages, _ptr(status),
+        _stream()))
+    return status
 
 
 def mla_decode_plan_host(seqlens, s_q, h_q, h_kv=1, head_dim_v=MLA_DV, num_cus=256):

@@ -42,6 +42,7 @@ _SIGS = {
     "mla_kv_append_fp8": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P],
     "mla_kv_quantize_fp8": [_P, _P, _P, ctypes.c_int64, _P],
     "mla_decode_plan_host": [_P, _I, _I, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PlanInfo)],
+    "mla_check_pages": [_P, _P, _I, _I, _I, _P, _P],
     "mla_status_string": [ctypes.c_int],
     "mla_profile_events": [_P, _P],
 }

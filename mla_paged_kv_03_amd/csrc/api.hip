@@ -446,6 +446,19 @@ int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q
   return MLA_OK;
 }
 
+int mla_check_pages(const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
+                    int32_t num_pages, int32_t max_pages_per_seq, int32_t* status,
+                    hipStream_t stream) {
+  if (!status) return MLA_ERR_NULL_ARG;
+  if (batch < 0 || num_pages < 1 || max_pages_per_seq < 1) return MLA_ERR_BAD_SHAPE;
+  if (batch > 0 && (!block_table || !cache_seqlens)) return MLA_ERR_NULL_ARG;
+  if (((uintptr_t)status & 3) != 0) return MLA_ERR_BAD_SHAPE;
+  if (mla::launch_check_pages(block_table, cache_seqlens, batch, num_pages, max_pages_per_seq,
+                              status, stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 void mla_profile_events(void* start, void* stop) {
   g_prof_start = (hipEvent_t)start;
   g_prof_stop = (hipEvent_t)stop;

@@ -202,4 +202,82 @@ hipError_t launch_combine_kernel(const CombineArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Check of the decode calls' device-side preconditions, one workgroup: every
+// thread scans a strided share of the (sequence, page) pairs, a length that
+// the block table cannot hold counting as page -1 of its sequence. The
+// workgroup reduces the violation count and the smallest linear index
+// b * (max_pages + 1) + (j + 1) and one thread stores both, so status needs
+// no initialisation. Block-table entries are read only for pages a valid
+// length uses.
+constexpr int CHECK_THREADS = 1024;
+
+__global__ __launch_bounds__(CHECK_THREADS) void check_pages_kernel(
+    const int32_t* block_table, const int32_t* seqlens, int B, int num_pages, int max_pages,
+    int bt_stride, int32_t* status) {
+  __shared__ int s_count[CHECK_THREADS / 64];
+  __shared__ int64_t s_first[CHECK_THREADS / 64];
+  const int64_t per_seq = (int64_t)max_pages + 1;
+  const int64_t n = (int64_t)B * per_seq;
+  int count = 0;
+  int64_t first = INT64_MAX;
+  for (int64_t i = threadIdx.x; i < n; i += CHECK_THREADS) {
+    const int b = (int)(i / per_seq);
+    const int j = (int)(i - (int64_t)b * per_seq) - 1;  // -1: the length itself
+    const int L = seqlens[b];
+    const bool len_ok = L >= 0 && (int64_t)L <= 64 * (int64_t)max_pages;
+    bool bad;
+    if (j < 0) {
+      bad = !len_ok;
+    } else {
+      bad = false;
+      if (len_ok && j < (L + 63) / 64) {
+        const int page = block_table[(size_t)b * bt_stride + j];
+        bad = page < 0 || page >= num_pages;
+      }
+    }
+    if (bad) {
+      ++count;
+      first = first < i ? first : i;
+    }
+  }
+  // wave reductions, then one value per wave through LDS
+  for (int off = 32; off > 0; off >>= 1) {
+    count += __shfl_xor(count, off);
+    const int64_t o = __shfl_xor(first, off);
+    first = first < o ? first : o;
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) {
+    s_count[wv] = count;
+    s_first[wv] = first;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = 0;
+    int64_t f = INT64_MAX;
+    for (int w = 0; w < CHECK_THREADS / 64; ++w) {
+      c += s_count[w];
+      f = f < s_first[w] ? f : s_first[w];
+    }
+    status[0] = c;
+    if (f == INT64_MAX) {
+      status[1] = -1;
+      status[2] = 0;
+      status[3] = 0;
+    } else {
+      const int b = (int)(f / per_seq), j = (int)(f % per_seq) - 1;
+      status[1] = b;
+      status[2] = j;
+      status[3] = j < 0 ? seqlens[b] : block_table[(size_t)b * bt_stride + j];
+    }
+  }
+}
+
+hipError_t launch_check_pages(const int32_t* block_table, const int32_t* seqlens, int B,
+                              int num_pages, int max_pages, int32_t* status, hipStream_t st) {
+  hipLaunchKernelGGL(check_pages_kernel, dim3(1), dim3(CHECK_THREADS), 0, st, block_table, seqlens,
+                     B, num_pages, max_pages, max_pages, status);
+  return hipGetLastError();
+}
+
 }  // namespace mla

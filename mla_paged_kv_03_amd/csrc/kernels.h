@@ -97,6 +97,9 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t st);
 hipError_t launch_decode_kernel(const DecodeArgs& a, int nw, int kind, int grid, hipStream_t st);
 // Split-KV merge of the partial results of split sequences.
 hipError_t launch_combine_kernel(const CombineArgs& a, hipStream_t st);
+// Device-side precondition check of the decode calls (one workgroup).
+hipError_t launch_check_pages(const int32_t* block_table, const int32_t* seqlens, int B,
+                              int num_pages, int max_pages, int32_t* status, hipStream_t st);
 // Schedule: worker records and unit prefix into meta, slot prefix into slots.
 hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int32_t* meta,
                               int32_t* slots, hipStream_t st);

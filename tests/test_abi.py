@@ -22,7 +22,7 @@ def test_every_declared_function_is_exported(L):
     assert {"mla_decode_plan", "mla_decode", "gqa_decode", "attn_combine", "mla_kv_append",
             "gqa_kv_append", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output",
             "gqla_decode", "mla_decode_fp8", "mla_kv_append_fp8",
-            "mla_kv_quantize_fp8"} <= set(names)
+            "mla_kv_quantize_fp8", "mla_check_pages"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -83,6 +83,18 @@ def test_attn_combine_argument_checks(L):
     assert L.attn_combine(p, p, p, 2, 4, 12, p, p, None) == -2      # dv not a multiple of 8
     assert L.attn_combine(None, p, p, 2, 4, 16, p, p, None) == -1
     assert L.attn_combine(p, p, p, 0, 4, 16, p, p, None) == 0        # nothing to do
+
+
+def test_check_pages_argument_checks(L):
+    p = ctypes.c_void_p(64)
+    # block_table, cache_seqlens, batch, num_pages, max_pages, status, stream
+    assert L.mla_check_pages(p, p, 2, 10, 4, None, None) == -1          # no status word
+    assert L.mla_check_pages(None, p, 2, 10, 4, p, None) == -1
+    assert L.mla_check_pages(p, None, 2, 10, 4, p, None) == -1
+    assert L.mla_check_pages(p, p, -1, 10, 4, p, None) == -2
+    assert L.mla_check_pages(p, p, 2, 0, 4, p, None) == -2
+    assert L.mla_check_pages(p, p, 2, 10, 0, p, None) == -2
+    assert L.mla_check_pages(p, p, 2, 10, 4, ctypes.c_void_p(66), None) == -2
 
 
 def test_kv_append_argument_checks(L):
