@@ -130,6 +130,21 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
   const int s0 = a.slots[b];
   const int ns = a.slots[b + 1] - s0;
   if (ns <= 0) return;
+  const float* po = a.part_o + ((size_t)s0 * a.R + rho) * a.DV;
+  const size_t pstride = (size_t)a.R * a.DV;
+  auto load = [&](int i, int k) -> f32x4 {
+    const int c = lane * 4 + 256 * k;
+    return c < a.DV ? *(const f32x4*)(po + (size_t)i * pstride + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // the first two partial rows are loaded together with the lse values
+  // rather than after the weights are known (one memory round trip less)
+  const bool two = ns >= 2;
+  f32x4 y0[NK], y1[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    y0[k] = load(0, k);
+    y1[k] = two ? load(1, k) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   const float* pl = a.part_lse + (size_t)s0 * a.R + rho;
   // lane i (and i + 64, ...) holds partial i's lse
   const float mine = lane < ns ? pl[(size_t)lane * a.R] : -INFINITY;
@@ -150,16 +165,13 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
   auto weight = [&](int i) -> float {
     return i < 64 ? __shfl(myw, i) : fast_exp2((pl[(size_t)i * a.R] - mx) * LOG2E) * inv;
   };
-  const float* po = a.part_o + ((size_t)s0 * a.R + rho) * a.DV;
-  const size_t pstride = (size_t)a.R * a.DV;
-  auto load = [&](int i, int k) -> f32x4 {
-    const int c = lane * 4 + 256 * k;
-    return c < a.DV ? *(const f32x4*)(po + (size_t)i * pstride + c) : f32x4{0.f, 0.f, 0.f, 0.f};
-  };
   f32x4 acc[NK];
+  {
+    const float w0 = weight(0), w1 = two ? weight(1) : 0.f;
 #pragma unroll
-  for (int k = 0; k < NK; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int i = 0;
+    for (int k = 0; k < NK; ++k) acc[k] = w0 * y0[k] + w1 * y1[k];
+  }
+  int i = two ? 2 : 1;
   for (; i + 2 <= ns; i += 2) {
     f32x4 x0[NK], x1[NK];
 #pragma unroll
