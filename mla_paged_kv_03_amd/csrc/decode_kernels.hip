@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
   static_assert(LY::DMA_PER_TILE % NW == 0 && NDMA < 64, "page copies split evenly");
 
   // the page buffers, reused at the end of a range for the key-part merge
-  constexpr int MERGE_BYTES = (KS - 1) * R * (NCB * 4 + 2) * 64 * 4;
+  constexpr int MERGE_BYTES = (KS - 1) * R * (NCB * 4 + 3) * 64 * 4;
   constexpr int NB = PPT == 2 ? 2 : LY::NBUF;  // buffers of PPT pages each
   constexpr int STEP_BYTES = PPT * LY::TILE;
   constexpr int LDS_BYTES = NB * STEP_BYTES > MERGE_BYTES ? NB * STEP_BYTES : MERGE_BYTES;
@@ -273,14 +273,19 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
     // REF_LIMIT, which it reports. Otherwise: the lazily rescaled online
     // softmax, which cannot overflow. The fixed pass touches O with MFMA
     // only, so O stays in the accumulator registers.
+    // l sums the weights as computed (for the LSE); lw sums them as the P V
+    // MFMA receives them, rounded to bf16, and normalises the output, whose
+    // weights then form an exact convex combination (with FP8 the weights
+    // carry power-of-two token scales, which commute with the rounding)
     f32x4 o[NCB];
-    float m, l;
+    float m, l, lw;
     auto run_range = [&](auto fixed_tag) -> bool {
     constexpr bool FIXED = decltype(fixed_tag)::value;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     m = -INFINITY;
     l = 0.f;
+    lw = 0.f;
     bool over = false;
 
     // a step's PPT pages from page j into buffer buf; past the worker's
@@ -392,13 +397,14 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
           // key yet has m = -inf, and exp2(m - m) would be NaN)
           const float alpha = need ? fast_exp2(m - tmax) : 1.f;  // 0 when m = -inf
           l *= alpha;
+          lw *= alpha;
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
           m = need ? tmax : m;
         }
       }
       const float m_use = m == -INFINITY ? 0.f : m;
-      float psum = 0.f;
+      float psum = 0.f, wsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -407,8 +413,10 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
           // FP8: the V row is scaled by its token scale too; l is not
           s[kb][i] = LY::FP8 ? p * ksc[kb][i] : p;
           psum += p;
+          wsum += (float)(__bf16)p;
         }
       l += sum4groups(psum);
+      lw += sum4groups(wsum);
 
       // O^T += V^T . P^T
       if constexpr (KW >= 32) {
@@ -536,8 +544,8 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
     // merge the key parts of each row group through LDS (page buffers are
     // free: every copy has landed and every wave has passed the last barrier)
     if constexpr (KS > 1) {
-      float* red = (float*)lds;  // [KS-1][R][NCB*4 + 2][64] floats
-      constexpr int PER = NCB * 4 + 2;
+      float* red = (float*)lds;  // [KS-1][R][NCB*4 + 3][64] floats
+      constexpr int PER = NCB * 4 + 3;
       static_assert((KS - 1) * R * PER * 64 * 4 <= LDS_BYTES, "the merge fits in LDS");
       if (ks > 0) {
         float* my = red + ((ks - 1) * R + rg) * PER * 64 + lane;
@@ -547,6 +555,7 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
           for (int i = 0; i < 4; ++i) my[(cb * 4 + i) * 64] = o[cb][i];
         my[(NCB * 4) * 64] = m;
         my[(NCB * 4 + 1) * 64] = l;
+        my[(NCB * 4 + 2) * 64] = lw;
       }
       __syncthreads();
       if (ks == 0) {
@@ -558,6 +567,7 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
           const float mu = mm == -INFINITY ? 0.f : mm;
           const float a1 = fast_exp2(m - mu), a2 = fast_exp2(m2 - mu);
           l = a1 * l + a2 * l2;
+          lw = a1 * lw + a2 * ot[(NCB * 4 + 2) * 64];
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -570,7 +580,7 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
 
     // epilogue: normalise; lane l holds dv = 16cb + 4(l/16) + i
     if (!CW && row_ok && ks == 0) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = lw > 0.f ? 1.f / lw : 0.f;
     const float lse_v = l > 0.f ? (m + __log2f(l)) * LN2 : -INFINITY;
     if (nslots == 0) {
       uint16_t* orow = a.out + ((size_t)b * TH + rho) * DV;

@@ -34,6 +34,11 @@ SMALL = {
     # causal masking some rows of a wave see a key while others see none yet
     "mla_h40_t2_causal": _mla(10, 2, 40, RAGGED, True),
     "mla_h128_t1_kvhalf": _mla(4, 1, 128, (4096, 100, 3000, 1), False, kv_std=0.5),
+    # many short sequences at 64-row blocks: a worker's range crosses many
+    # sequences, empty ones included, and the copy waves' and compute waves'
+    # sequence loops must stay in step through all of them
+    "mla_h128_t1_many_short": _mla(300, 1, 128, (RAGGED[:8] * 38)[:300], False),
+    "mla_h64_t2_many_short_causal": _mla(300, 2, 64, (RAGGED[1:9] * 38)[:300], True),
     "gqa_h128_g8": _gqa(10, 1, 128, 8, RAGGED),
     "gqa_h16_g2": _gqa(10, 1, 16, 2, RAGGED),
     "gqa_h8_g8": _gqa(10, 1, 8, 8, RAGGED),
