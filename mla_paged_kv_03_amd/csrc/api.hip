@@ -397,25 +397,28 @@ int gqla_expand_kv(const void* kv_rows, const void* w_uk, const void* w_uv, void
   if (!aligned16(kv_rows) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(k_rows) ||
       !aligned16(v_rows))
     return MLA_ERR_BAD_SHAPE;
-  mla::GemmArgs a = {};
+  static_assert(GQLA_DH == 128 && GQLA_DVG == 128 && GQLA_DC == 512, "expansion kernel widths");
+  mla::ExpandArgs a = {};
   a.a = (const uint16_t*)kv_rows;
-  a.inner = 1;
-  a.a_outer = GQLA_DC + GQLA_DR;
-  a.b_batch = (int64_t)GQLA_DC * GQLA_DH; a.ldb = GQLA_DH; a.b_kn = 1;
-  a.M = (int)n_rows; a.N = GQLA_DH; a.K = GQLA_DC; a.batches = h_kv;
+  a.M = n_rows;
+  a.G = h_kv;
+  // workgroups: about one per CU, in slices of 8 (one per XCD) per group
+  int cus = 0;
+  if (device_cus(&cus) != MLA_OK) return MLA_ERR_HIP;
+  const int per_group = (cus + h_kv - 1) / h_kv;
+  a.n_slices = 8 * ((per_group + 7) / 8);
   // K: group g's columns 0..127 of each expanded row, plus the shared rope
-  a.b = (const uint16_t*)w_uk;
+  a.w = (const uint16_t*)w_uk;
   a.c = (uint16_t*)k_rows;
   a.c_outer = (int64_t)h_kv * GQLA_DQ; a.c_batch = GQLA_DQ;
-  a.rope = 1; a.rope_a_off = GQLA_DC; a.rope_c_off = GQLA_DH;
-  if (mla::launch_gemm(a, stream) != hipSuccess) return MLA_ERR_HIP;
+  a.rope = 1; a.rope_c_off = GQLA_DH;
+  if (mla::launch_expand(a, stream) != hipSuccess) return MLA_ERR_HIP;
   // V
-  a.b = (const uint16_t*)w_uv;
-  a.b_batch = (int64_t)GQLA_DC * GQLA_DVG; a.ldb = GQLA_DVG; a.N = GQLA_DVG;
+  a.w = (const uint16_t*)w_uv;
   a.c = (uint16_t*)v_rows;
   a.c_outer = (int64_t)h_kv * GQLA_DVG; a.c_batch = GQLA_DVG;
   a.rope = 0;
-  return mla::launch_gemm(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return mla::launch_expand(a, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q, int32_t h_q,

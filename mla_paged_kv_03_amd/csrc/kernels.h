@@ -76,6 +76,18 @@ struct GemmArgs {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
+// GQLA cache expansion: C[m, g, 0:128] = A[m, 0:512] W_g (A rows of 576
+// bf16, W [G][512][128]); with rope, also C[m, g, rope_c_off + j] =
+// A[m, 512 + j] for j < 64. Grid G * n_slices (n_slices a multiple of 8).
+struct ExpandArgs {
+  const uint16_t* a;      // [M, 576]
+  const uint16_t* w;      // [G, 512, 128]
+  uint16_t* c;            // row m, group g at c + m * c_outer + g * c_batch
+  int64_t M, c_outer;
+  int G, c_batch, rope, rope_c_off, n_slices;
+};
+hipError_t launch_expand(const ExpandArgs& a, hipStream_t st);
+
 // FP8 quantisation of 576-wide bf16 latent rows: row r of src (r < B * T)
 // goes to row r of dst (block_table null), or, as an append, to the slot of
 // new token t = r % T of sequence b = r / T (same rule as AppendArgs).
