@@ -39,6 +39,10 @@ SMALL = {
     # sequence loops must stay in step through all of them
     "mla_h128_t1_many_short": _mla(300, 1, 128, (RAGGED[:8] * 38)[:300], False),
     "mla_h64_t2_many_short_causal": _mla(300, 2, 64, (RAGGED[1:9] * 38)[:300], True),
+    # one sequence over every worker: 128 partial results per row to merge
+    "mla_h16_t1_one_long": _mla(1, 1, 16, (16384,), False),
+    "mla_h128_t2_causal_long": _mla(3, 2, 128, (20000, 3, 700), True),
+    "gqa_h16_g2_one_long": _gqa(1, 1, 16, 2, (30000,)),
     "gqa_h128_g8": _gqa(10, 1, 128, 8, RAGGED),
     "gqa_h16_g2": _gqa(10, 1, 16, 2, RAGGED),
     "gqa_h8_g8": _gqa(10, 1, 8, 8, RAGGED),
@@ -103,7 +107,8 @@ def test_nan_in_page_tails_and_pads_is_never_read(dev, name):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-@pytest.mark.parametrize("name", ["mla_h128_t2_causal", "gqa_h32_g4_t2_causal"])
+@pytest.mark.parametrize("name", ["mla_h128_t2_causal", "gqa_h32_g4_t2_causal",
+                                  "mla_h16_t1_one_long"])
 def test_page_permutation_and_rerun_are_bitwise_equal(dev, name):
     cfg = SMALL[name]
     d = inputs(cfg, seed=6)
@@ -198,6 +203,30 @@ def test_device_plan_equals_host_plan(dev):
         meta, splits, info = lib.mla_decode_plan_host(Ls, T, H, G, dv, num_cus=cus)
         assert np.array_equal(plan.sched_metadata.cpu().numpy(), meta)
         assert np.array_equal(plan.num_splits.cpu().numpy(), splits)
+
+
+@pytest.mark.parametrize("name", ["mla_h128_t2_causal_long", "gqa_h16_g2_one_long"])
+def test_plan_reuse_is_exact(dev, name):
+    """One plan serves several decode calls (the layers of a step): every
+    call gives the same bits and leaves the plan as the plan kernel wrote
+    it."""
+    import torch
+    import mla_paged_kv_03_amd as lib
+    cfg = SMALL[name]
+    d = inputs(cfg, seed=7)
+    t = to_device(d, dev)
+    G = cfg.h_kv if cfg.kind == "gqa" else 1
+    dv = 512 if cfg.kind == "mla" else 128
+    plan = lib.mla_decode_plan(t["cache_seqlens"], cfg.s_q, cfg.h_q, G, dv)
+    runs = [run_gpu(d, t, plan=plan) for _ in range(3)]
+    for o, l in runs[1:]:
+        assert np.array_equal(o, runs[0][0]) and np.array_equal(l, runs[0][1])
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    meta, splits, info = lib.mla_decode_plan_host(list(d["cache_seqlens"]), cfg.s_q, cfg.h_q, G,
+                                                  dv, num_cus=cus)
+    assert np.array_equal(plan.sched_metadata.cpu().numpy(), meta)
+    ref_out, ref_lse = run_oracle(d)
+    check(runs[0][0], runs[0][1], ref_out, ref_lse, name)
 
 
 def test_attn_combine_matches_oracle_combine(dev):
