@@ -103,12 +103,21 @@ hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int32_t* met
 
 // Merge the partials of one (sequence, row): lse = m + ln sum exp(lse_i - m),
 // out = sum exp(lse_i - lse) o_i. One wave per row, four rows per
-// workgroup; grid (ceil(R / 4), B). Lane i holds partial i's lse (the max
+// workgroup; grid (ceil(R / 4), B, Z). Lane i holds item i's lse (the max
 // and sum are wave reductions); lane l owns columns 4l + 256k, k < NK, and
-// reads two partial rows before summing them, so independent loads are in
+// reads four items' rows before summing them, so independent loads are in
 // flight together while the register count stays low enough for eight
 // waves per SIMD.
+//
+// Items: level 0 merges every partial of the sequence. A sequence spread
+// over many workgroups (one long sequence in a small batch) has up to one
+// partial per worker, too many for one wave to walk in order, so the merge
+// then takes two launches: level 1 (z = blockIdx.z) merges the z-th chunk of
+// ceil(n / Z) consecutive partials into the chunk's first slot, level 2
+// merges the chunks' results. Both orders are fixed, so results do not
+// depend on timing.
 constexpr int COMBINE_ROWS = 4;
+constexpr int COMBINE_UNROLL = 4;
 
 __device__ __forceinline__ float wave_max64(float x) {
 #pragma unroll
@@ -123,6 +132,7 @@ __device__ __forceinline__ float wave_sum64(float x) {
 
 template <int NK>
 __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs a) {
+  constexpr int U = COMBINE_UNROLL;
   const int lane = threadIdx.x & 63;
   const int rho = blockIdx.x * COMBINE_ROWS + (threadIdx.x >> 6);
   const int b = blockIdx.y;
@@ -130,86 +140,136 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
   const int s0 = a.slots[b];
   const int ns = a.slots[b + 1] - s0;
   if (ns <= 0) return;
-  const float* po = a.part_o + ((size_t)s0 * a.R + rho) * a.DV;
-  const size_t pstride = (size_t)a.R * a.DV;
+  // this wave's items: slots s0 + first + i * stride, i < n
+  int first = 0, stride = 1, n = ns;
+  if (a.level != 0) {
+    const int c = (ns + a.Z - 1) / a.Z;  // chunk length
+    if (a.level == 1) {
+      first = blockIdx.z * c;
+      n = min(c, ns - first);
+      if (c <= 1 || n <= 0) return;  // c = 1: the partials are the chunks' results
+    } else if (c > 1) {
+      stride = c;
+      n = (ns + c - 1) / c;
+    }
+  }
+  const bool final = a.level != 1;
+  const size_t row = (size_t)(s0 + first) * a.R + rho;
+  const float* po = a.part_o + row * a.DV;
+  const float* pl = a.part_lse + row;
+  const size_t ostride = (size_t)stride * a.R * a.DV, lstride = (size_t)stride * a.R;
   auto load = [&](int i, int k) -> f32x4 {
     const int c = lane * 4 + 256 * k;
-    return c < a.DV ? *(const f32x4*)(po + (size_t)i * pstride + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    return c < a.DV ? *(const f32x4*)(po + (size_t)i * ostride + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   };
-  // the first two partial rows are loaded together with the lse values
-  // rather than after the weights are known (one memory round trip less)
-  const bool two = ns >= 2;
-  f32x4 y0[NK], y1[NK];
+  // the first U items' rows are loaded together with the lse values rather
+  // than after the weights are known (one memory round trip less)
+  f32x4 y[U][NK];
 #pragma unroll
-  for (int k = 0; k < NK; ++k) {
-    y0[k] = load(0, k);
-    y1[k] = two ? load(1, k) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  const float* pl = a.part_lse + (size_t)s0 * a.R + rho;
-  // lane i (and i + 64, ...) holds partial i's lse
-  const float mine = lane < ns ? pl[(size_t)lane * a.R] : -INFINITY;
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int k = 0; k < NK; ++k) y[u][k] = u < n ? load(u, k) : f32x4{0.f, 0.f, 0.f, 0.f};
+  // lane i (and i + 64, ...) holds item i's lse
+  const float mine = lane < n ? pl[(size_t)lane * lstride] : -INFINITY;
   float mx = mine;
-  for (int i = lane + 64; i < ns; i += 64) mx = fmaxf(mx, pl[(size_t)i * a.R]);
+  for (int i = lane + 64; i < n; i += 64) mx = fmaxf(mx, pl[(size_t)i * lstride]);
   mx = wave_max64(mx);
-  uint16_t* orow = a.out + ((size_t)b * a.R + rho) * a.DV;
   if (mx == -INFINITY) {
-    for (int c = lane * 4; c < a.DV; c += 64 * 4) *(u32x2*)(orow + c) = u32x2{0u, 0u};
-    if (lane == 0) a.lse[(size_t)b * a.R + rho] = -INFINITY;
+    // no key at all: out = 0, lse = -inf (also as a chunk's result)
+    if (final) {
+      uint16_t* orow = a.out + ((size_t)b * a.R + rho) * a.DV;
+      for (int c = lane * 4; c < a.DV; c += 64 * 4) *(u32x2*)(orow + c) = u32x2{0u, 0u};
+      if (lane == 0) a.lse[(size_t)b * a.R + rho] = -INFINITY;
+    } else {
+      float* crow = a.chunk_o + row * a.DV;
+      for (int c = lane * 4; c < a.DV; c += 64 * 4) *(f32x4*)(crow + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (lane == 0) a.chunk_lse[row] = -INFINITY;
+    }
     return;
   }
-  float tot = lane < ns ? fast_exp2((mine - mx) * LOG2E) : 0.f;
-  for (int i = lane + 64; i < ns; i += 64) tot += fast_exp2((pl[(size_t)i * a.R] - mx) * LOG2E);
+  float tot = lane < n ? fast_exp2((mine - mx) * LOG2E) : 0.f;
+  for (int i = lane + 64; i < n; i += 64) tot += fast_exp2((pl[(size_t)i * lstride] - mx) * LOG2E);
   tot = wave_sum64(tot);
   const float inv = 1.f / tot;
-  const float myw = lane < ns ? fast_exp2((mine - mx) * LOG2E) * inv : 0.f;
+  const float myw = lane < n ? fast_exp2((mine - mx) * LOG2E) * inv : 0.f;
   auto weight = [&](int i) -> float {
-    return i < 64 ? __shfl(myw, i) : fast_exp2((pl[(size_t)i * a.R] - mx) * LOG2E) * inv;
+    return i < 64 ? __shfl(myw, i) : fast_exp2((pl[(size_t)i * lstride] - mx) * LOG2E) * inv;
   };
   f32x4 acc[NK];
   {
-    const float w0 = weight(0), w1 = two ? weight(1) : 0.f;
+    float w[U];
 #pragma unroll
-    for (int k = 0; k < NK; ++k) acc[k] = w0 * y0[k] + w1 * y1[k];
-  }
-  int i = two ? 2 : 1;
-  for (; i + 2 <= ns; i += 2) {
-    f32x4 x0[NK], x1[NK];
+    for (int u = 0; u < U; ++u) w[u] = u < n ? weight(u) : 0.f;
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
-      x0[k] = load(i, k);
-      x1[k] = load(i + 1, k);
-    }
-    const float w0 = weight(i), w1 = weight(i + 1);
+      acc[k] = w[0] * y[0][k];
 #pragma unroll
-    for (int k = 0; k < NK; ++k) acc[k] += w0 * x0[k] + w1 * x1[k];
-  }
-  if (i < ns) {
-    const float w0 = weight(i);
-#pragma unroll
-    for (int k = 0; k < NK; ++k) acc[k] += w0 * load(i, k);
-  }
-#pragma unroll
-  for (int k = 0; k < NK; ++k) {
-    const int c = lane * 4 + 256 * k;
-    if (c < a.DV) {
-      u32x2 y;
-      y[0] = pack_bf16x2(acc[k][0], acc[k][1]);
-      y[1] = pack_bf16x2(acc[k][2], acc[k][3]);
-      *(u32x2*)(orow + c) = y;
+      for (int u = 1; u < U; ++u) acc[k] += w[u] * y[u][k];
     }
   }
-  if (lane == 0) a.lse[(size_t)b * a.R + rho] = mx + __logf(tot);
+  for (int i = U; i < n; i += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < NK; ++k) y[u][k] = i + u < n ? load(i + u, k) : f32x4{0.f, 0.f, 0.f, 0.f};
+    float w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = i + u < n ? weight(i + u) : 0.f;
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[k] += w[u] * y[u][k];
+  }
+  const float lse_v = mx + __logf(tot);
+  if (final) {
+    uint16_t* orow = a.out + ((size_t)b * a.R + rho) * a.DV;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int c = lane * 4 + 256 * k;
+      if (c < a.DV) {
+        u32x2 z;
+        z[0] = pack_bf16x2(acc[k][0], acc[k][1]);
+        z[1] = pack_bf16x2(acc[k][2], acc[k][3]);
+        *(u32x2*)(orow + c) = z;
+      }
+    }
+    if (lane == 0) a.lse[(size_t)b * a.R + rho] = lse_v;
+  } else {
+    // over the chunk's first item, whose row this wave has already read
+    float* crow = a.chunk_o + row * a.DV;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int c = lane * 4 + 256 * k;
+      if (c < a.DV) *(f32x4*)(crow + c) = acc[k];
+    }
+    if (lane == 0) a.chunk_lse[row] = lse_v;
+  }
+}
+
+template <int NK>
+static void launch_combine_nk(CombineArgs a, hipStream_t st) {
+  const dim3 block(64 * COMBINE_ROWS);
+  const unsigned gx = (a.R + COMBINE_ROWS - 1) / COMBINE_ROWS;
+  if (a.Z <= 1) {
+    a.level = 0;
+    hipLaunchKernelGGL(combine_kernel<NK>, dim3(gx, a.B), block, 0, st, a);
+    return;
+  }
+  a.level = 1;
+  hipLaunchKernelGGL(combine_kernel<NK>, dim3(gx, a.B, a.Z), block, 0, st, a);
+  a.level = 2;
+  hipLaunchKernelGGL(combine_kernel<NK>, dim3(gx, a.B), block, 0, st, a);
 }
 
 hipError_t launch_combine_kernel(const CombineArgs& a, hipStream_t st) {
   if (a.B <= 0 || a.R <= 0) return hipSuccess;
-  if (a.DV > 1024 || a.B > 65535) return hipErrorInvalidValue;
-  const dim3 grid((a.R + COMBINE_ROWS - 1) / COMBINE_ROWS, a.B), block(64 * COMBINE_ROWS);
+  if (a.DV > 1024 || a.B > 65535 || a.Z > 65535) return hipErrorInvalidValue;
+  if (a.Z > 1 && (!a.chunk_o || !a.chunk_lse)) return hipErrorInvalidValue;
   const int nk = (a.DV + 255) / 256;
   switch (nk) {
-    case 1: hipLaunchKernelGGL(combine_kernel<1>, grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, st, a); break;
-    default: hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, st, a); break;
+    case 1: launch_combine_nk<1>(a, st); break;
+    case 2: launch_combine_nk<2>(a, st); break;
+    default: launch_combine_nk<4>(a, st); break;
   }
   return hipGetLastError();
 }

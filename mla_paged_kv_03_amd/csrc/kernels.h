@@ -42,6 +42,13 @@ struct CombineArgs {
   uint16_t* out;               // [B][R][DV]
   float* lse;                  // [B][R]
   int B, R, DV;
+  // Merge in one pass (level 0), or in two launches for sequences with many
+  // partials: level 1 merges chunk z < Z of ceil(n / Z) consecutive partials
+  // into the chunk's first slot of chunk_o / chunk_lse (the same buffers as
+  // part_o / part_lse), level 2 merges the chunks' results into out / lse.
+  int level, Z;
+  float* chunk_o;
+  float* chunk_lse;
 };
 
 struct AppendArgs {
@@ -107,7 +114,8 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t st);
 
 // One decode launch: grid = workers * row blocks, 64 * nw threads.
 hipError_t launch_decode_kernel(const DecodeArgs& a, int nw, int kind, int grid, hipStream_t st);
-// Split-KV merge of the partial results of split sequences.
+// Split-KV merge of the partial results of split sequences (one level, or
+// the two launches of levels 1 and 2 when a.Z > 1).
 hipError_t launch_combine_kernel(const CombineArgs& a, hipStream_t st);
 // Device-side precondition check of the decode calls (one workgroup).
 hipError_t launch_check_pages(const int32_t* block_table, const int32_t* seqlens, int B,
