@@ -26,10 +26,13 @@ __device__ __forceinline__ void decode_block_id(int bid, int W, int RB, int& w, 
 }
 
 // Waves per decode workgroup: four compute waves, plus four copy waves for
-// the bf16 latent cache at 64 query rows per workgroup, where every page is
-// copied once per row block and the copies cost the compute waves as much
-// time as the products when they issue them themselves.
-constexpr int decode_waves(int R, int KIND) { return (KIND == KIND_MLA && R == 4) ? 8 : 4; }
+// the latent cache at 64 query rows per workgroup (bf16, or FP8 pages that
+// the copy waves dequantise to bf16), where every page is copied once per
+// row block and the copies cost the compute waves as much time as the
+// products when they issue them themselves.
+constexpr int decode_waves(int R, int KIND) {
+  return ((KIND == KIND_MLA || KIND == KIND_MLA_FP8) && R == 4) ? 8 : 4;
+}
 
 // LDS page layouts (bytes). Row k of a page keeps its 16-byte chunk c at
 // k * PITCH + 16 * (c ^ xor(k)). Measured on gfx950 (whose LDS serves 256
@@ -149,6 +152,13 @@ template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
+// The same two codes times s, rounded to bf16 (to nearest even) by the
+// conversion itself; with a power-of-two s the product is exact inside the
+// bf16 range.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2_scaled(uint32_t w, float s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, HI));
+}
 __device__ __forceinline__ bf16x8 fp8x8_bf16x8(uint32_t w0, uint32_t w1) {
   const u32x4 u = {fp8x2_bf16x2<false>(w0), fp8x2_bf16x2<true>(w0), fp8x2_bf16x2<false>(w1),
                    fp8x2_bf16x2<true>(w1)};
@@ -171,6 +181,7 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Keeps the compiler from moving memory operations across this point (it
 // bounds how far LDS reads are hoisted ahead of the MFMAs that use them).

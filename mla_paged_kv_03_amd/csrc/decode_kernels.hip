@@ -19,7 +19,9 @@
 //     states, merged through LDS when the worker's range of a sequence ends.
 //   * Pages stream HBM -> LDS with global_load_lds_dwordx4 (no staging
 //     registers), double-buffered: the next page is in flight while the
-//     current one is computed.
+//     current one is computed. FP8 pages at 64 rows per workgroup instead
+//     pass through the copy waves' registers, which dequantise them into
+//     the bf16 latent layout.
 //   * Scores are computed transposed, S^T[key][row] = K . Q^T, on 16x16x32
 //     bf16 MFMA: lane l holds query row l % 16 and four keys per 16-key
 //     block, so the row max and sum are in-lane reductions plus two
@@ -40,8 +42,12 @@ namespace mla {
 
 template <int R, int KIND>
 __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(DecodeArgs a) {
-  using LY = Layout<KIND>;
-  constexpr bool GQA = KIND != KIND_MLA;
+  // FP8 pages at 64 rows per workgroup: the copy waves dequantise every page
+  // into the bf16 latent layout (each code times its token's power-of-two
+  // scale, exact), so the compute waves run the bf16 path unchanged
+  constexpr bool DEQ = KIND == KIND_MLA_FP8 && R == 4;
+  using LY = Layout<DEQ ? KIND_MLA : KIND>;
+  constexpr bool GQA = KIND != KIND_MLA && !DEQ;
   constexpr int NW = 4;           // compute waves
   // With copy waves, waves NW .. 2NW-1 issue every page copy and compute
   // nothing, so the compute waves never stall behind the address unit.
@@ -186,6 +192,45 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
     if (p0 >= p1) continue;
     const int split = b == bs ? rec[sched::R_SPLIT0] : 0;
     const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+
+    // FP8 pages through the copy waves' registers: 16-byte unit u = 64i +
+    // lane (i = cw + NW t) holds codes 16x .. 16x + 15 of row r = u / 36,
+    // x = u % 36, which become bf16 chunks 2x and 2x + 1 of LDS row r; rows
+    // past the sequence end repeat its last row, scale included
+    constexpr int DQ_T = DEQ ? 36 / NW : 1;
+    auto load_codes = [&](int j, u32x4 (&dq)[DQ_T], float& scale) {
+      const int page = sload(uniform_ptr(bt + j));
+      const int nv = uniform(min(64, L - 64 * j));
+      const char* pbase = uniform_ptr((const char*)a.k + (size_t)page * (64 * 576));
+#pragma unroll
+      for (int t = 0; t < DQ_T; ++t) {
+        const int u = 64 * (cw + NW * t) + lane;
+        const int r = u / 36, x = u - 36 * r;
+        dq[t] = __builtin_nontemporal_load((const u32x4*)(pbase + min(r, nv - 1) * 576 + 16 * x));
+      }
+      scale = a.kscale[(size_t)page * 64 + min(lane, nv - 1)];
+    };
+    auto store_page = [&](const u32x4 (&dq)[DQ_T], float scale, int buf) {
+      lds_char* const dst = lds_p + buf * STEP_BYTES;
+#pragma unroll
+      for (int t = 0; t < DQ_T; ++t) {
+        const int u = 64 * (cw + NW * t) + lane;
+        const int r = u / 36, x = u - 36 * r;
+        const float sc = __shfl(scale, r);  // lane r holds row r's scale
+        u32x4 c0, c1;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          c0[2 * k] = fp8x2_bf16x2_scaled<false>(dq[t][k], sc);
+          c0[2 * k + 1] = fp8x2_bf16x2_scaled<true>(dq[t][k], sc);
+          c1[2 * k] = fp8x2_bf16x2_scaled<false>(dq[t][k + 2], sc);
+          c1[2 * k + 1] = fp8x2_bf16x2_scaled<true>(dq[t][k + 2], sc);
+        }
+        const int y = r & 7;
+        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+        *(lds_u32x4*)(dst + r * LY::K_PITCH + 16 * ((2 * x) ^ y)) = c0;
+        *(lds_u32x4*)(dst + r * LY::K_PITCH + 16 * ((2 * x + 1) ^ y)) = c1;
+      }
+    };
 
     // copy page j of sequence b to LDS byte dst
     auto issue_page = [&](int j, uint32_t dst) {
@@ -490,7 +535,31 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
       // other. At the barrier opening step j, step j's copies have landed
       // (each copy wave waited for its own) and step j - 1's compute is
       // done, so step j + 1 may refill that buffer.
-      if constexpr (CW) {
+      if constexpr (CW && DEQ) {
+        // two pages in registers (sets A and B by page parity): step j
+        // dequantises page j into buffer cur and sends out page j + 2's
+        // loads into the set it frees; the barrier opens page j once this
+        // wave's LDS writes are done
+        u32x4 dqa[DQ_T], dqb[DQ_T];
+        float sa = 0.f, sb = 0.f;
+        if (p0 < p1) load_codes(p0, dqa, sa);
+        if (p0 + 1 < p1) load_codes(p0 + 1, dqb, sb);
+        int cur = 0;
+        for (int j = p0; j < p1; j += 2) {
+          store_page(dqa, sa, cur);
+          if (j + 2 < p1) load_codes(j + 2, dqa, sa);
+          wait_lgkm0();
+          barrier();
+          cur ^= 1;
+          if (j + 1 < p1) {
+            store_page(dqb, sb, cur);
+            if (j + 3 < p1) load_codes(j + 3, dqb, sb);
+            wait_lgkm0();
+            barrier();
+            cur ^= 1;
+          }
+        }
+      } else if constexpr (CW) {
         if (p0 < p1) issue_step(p0, 0);
         int cur = 0;
         for (int j = p0; j < p1; ++j) {

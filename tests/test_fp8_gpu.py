@@ -153,21 +153,22 @@ def test_fp8_decode_reads_no_slot_past_the_end(dev):
     check(out, lse, ref_out, ref_lse, "fp8 decode poisoned")
 
 
-@pytest.mark.parametrize("period", [3, 5])
-def test_fp8_scores_climbing_from_page_to_page(dev, period):
+@pytest.mark.parametrize("period,heads", [(3, 16), (5, 16), (3, 64)])
+def test_fp8_scores_climbing_from_page_to_page(dev, period, heads):
     """Both softmax passes (fixed reference, then the rescaling fallback) on an
-    FP8 cache."""
+    FP8 cache, at 16 rows per KV head and at 64 (pages dequantised by the
+    copy waves, whose page loop then also runs twice)."""
     import mla_paged_kv_03_amd as lib
     import torch
     Ls = (64 * 300, 64 * 280 + 17, 64 * 300, 64 * 290)
-    cfg = _mla(4, 1, 16, Ls, False)
+    cfg = _mla(4, 1, heads, Ls, False)
     d = make_inputs(cfg, seed=12)
     _climbing_scores(d, cfg, period=period)
     codes, scales = fp8.quantize_cache(d["kv"])
-    log(f"[case] fp8 climbing scores period {period}")
+    log(f"[case] fp8 climbing scores period {period} heads {heads}")
     out, lse = _decode(d, codes, scales, dev)
     ref_out, ref_lse = _oracle(d, codes, scales)
-    check(out, lse, ref_out, ref_lse, f"fp8 climbing scores (period {period})")
+    check(out, lse, ref_out, ref_lse, f"fp8 climbing scores (period {period}, {heads} heads)")
 
 
 def _sample(cfg, L, k=4):
