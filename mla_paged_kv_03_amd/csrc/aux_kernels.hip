@@ -104,10 +104,11 @@ hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int32_t* met
 // Merge the partials of one (sequence, row): lse = m + ln sum exp(lse_i - m),
 // out = sum exp(lse_i - lse) o_i. One wave per row, four rows per
 // workgroup; grid (ceil(R / 4), B, Z). Lane i holds item i's lse (the max
-// and sum are wave reductions); lane l owns columns 4l + 256k, k < NK, and
-// reads four items' rows before summing them, so independent loads are in
-// flight together while the register count stays low enough for eight
-// waves per SIMD.
+// and sum are wave reductions); lane l owns columns 4l + 256k, k < NK. The
+// first two items' rows load with the lse values, later ones U at a time,
+// so independent loads are in flight together: two in the one-pass merge,
+// which keeps the registers low enough for eight waves per SIMD, four in
+// the two-launch merge of many partials.
 //
 // Items: level 0 merges every partial of the sequence. A sequence spread
 // over many workgroups (one long sequence in a small batch) has up to one
@@ -117,7 +118,6 @@ hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int32_t* met
 // merges the chunks' results. Both orders are fixed, so results do not
 // depend on timing.
 constexpr int COMBINE_ROWS = 4;
-constexpr int COMBINE_UNROLL = 4;
 
 __device__ __forceinline__ float wave_max64(float x) {
 #pragma unroll
@@ -130,9 +130,8 @@ __device__ __forceinline__ float wave_sum64(float x) {
   return x;
 }
 
-template <int NK>
+template <int NK, int U>
 __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs a) {
-  constexpr int U = COMBINE_UNROLL;
   const int lane = threadIdx.x & 63;
   const int rho = blockIdx.x * COMBINE_ROWS + (threadIdx.x >> 6);
   const int b = blockIdx.y;
@@ -162,11 +161,11 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
     const int c = lane * 4 + 256 * k;
     return c < a.DV ? *(const f32x4*)(po + (size_t)i * ostride + c) : f32x4{0.f, 0.f, 0.f, 0.f};
   };
-  // the first U items' rows are loaded together with the lse values rather
-  // than after the weights are known (one memory round trip less)
-  f32x4 y[U][NK];
+  // the first two items' rows are loaded together with the lse values
+  // rather than after the weights are known (one memory round trip less)
+  f32x4 y[2][NK];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int k = 0; k < NK; ++k) y[u][k] = u < n ? load(u, k) : f32x4{0.f, 0.f, 0.f, 0.f};
   // lane i (and i + 64, ...) holds item i's lse
@@ -197,28 +196,24 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
   };
   f32x4 acc[NK];
   {
-    float w[U];
+    const float w0 = weight(0), w1 = n > 1 ? weight(1) : 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = u < n ? weight(u) : 0.f;
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      acc[k] = w[0] * y[0][k];
-#pragma unroll
-      for (int u = 1; u < U; ++u) acc[k] += w[u] * y[u][k];
-    }
+    for (int k = 0; k < NK; ++k) acc[k] = w0 * y[0][k] + w1 * y[1][k];
   }
-  for (int i = U; i < n; i += U) {
+  // the rest U at a time, their loads in flight together
+  for (int i = 2; i < n; i += U) {
+    f32x4 x[U][NK];
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int k = 0; k < NK; ++k) y[u][k] = i + u < n ? load(i + u, k) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < NK; ++k) x[u][k] = i + u < n ? load(i + u, k) : f32x4{0.f, 0.f, 0.f, 0.f};
     float w[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) w[u] = i + u < n ? weight(i + u) : 0.f;
 #pragma unroll
     for (int k = 0; k < NK; ++k)
 #pragma unroll
-      for (int u = 0; u < U; ++u) acc[k] += w[u] * y[u][k];
+      for (int u = 0; u < U; ++u) acc[k] += w[u] * x[u][k];
   }
   const float lse_v = mx + __logf(tot);
   if (final) {
@@ -252,13 +247,13 @@ static void launch_combine_nk(CombineArgs a, hipStream_t st) {
   const unsigned gx = (a.R + COMBINE_ROWS - 1) / COMBINE_ROWS;
   if (a.Z <= 1) {
     a.level = 0;
-    hipLaunchKernelGGL(combine_kernel<NK>, dim3(gx, a.B), block, 0, st, a);
+    hipLaunchKernelGGL((combine_kernel<NK, 2>), dim3(gx, a.B), block, 0, st, a);
     return;
   }
   a.level = 1;
-  hipLaunchKernelGGL(combine_kernel<NK>, dim3(gx, a.B, a.Z), block, 0, st, a);
+  hipLaunchKernelGGL((combine_kernel<NK, 4>), dim3(gx, a.B, a.Z), block, 0, st, a);
   a.level = 2;
-  hipLaunchKernelGGL(combine_kernel<NK>, dim3(gx, a.B), block, 0, st, a);
+  hipLaunchKernelGGL((combine_kernel<NK, 4>), dim3(gx, a.B), block, 0, st, a);
 }
 
 hipError_t launch_combine_kernel(const CombineArgs& a, hipStream_t st) {
