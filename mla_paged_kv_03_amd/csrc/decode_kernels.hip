@@ -11,7 +11,8 @@
 // Shapes: the MQA-absorb and GQA decode paths of the GQLA review ("1. Key
 // Terms & Definitions").
 //
-// Work layout (gfx950, wave64, 4 waves per workgroup):
+// Work layout (gfx950, wave64, four compute waves per workgroup, plus four
+// copy waves for the latent cache at 64 rows per workgroup):
 //   * A workgroup owns one worker's range of pages (schedule.h) for one KV
 //     head g and a block of 16*R query rows that share that head. Wave w
 //     owns 16 rows (row group w % R); the KS = 4 / R waves of a row group
