@@ -1,6 +1,7 @@
 """The decode step captured in a HIP graph (torch.cuda.CUDAGraph): plan,
-decode and split merge, the paged append, the FP8 decode and the GQLA
-products record no allocation and no memset, so a captured step replays.
+decode and split merge (one launch or two), the paged append, the FP8
+decode (both page paths) and the GQLA products record no allocation and no
+memset, so a captured step replays.
 Each replay runs on fresh inputs copied into the captured buffers, with
 eager work in between, and must equal the eager result bit for bit."""
 import ctypes
@@ -14,20 +15,31 @@ from gpu_helpers import bf16_tensor, log
 pytestmark = pytest.mark.gpu
 
 
-def _mla_inputs(dev, seed):
+# mixed: 24 sequences, 2 causal tokens, 128 heads (the one-launch merge);
+# few_long: two long sequences over 16 heads, split over many workers (the
+# two-launch merge)
+MLA_SHAPES = {
+    "mixed": dict(batch=24, seqlen_rule="fixed",
+                  seqlens_fixed=tuple([1, 70, 640, 3000, 64, 0] * 4)),
+    "few_long": dict(batch=2, s_q=1, h_q=16, causal=False, seqlen_rule="fixed",
+                     seqlens_fixed=(20000, 9000)),
+}
+
+
+def _mla_inputs(dev, seed, shape="mixed"):
     import torch
-    cfg = CONFIGS[3].with_(batch=24, seqlen_rule="fixed",
-                           seqlens_fixed=tuple([1, 70, 640, 3000, 64, 0] * 4))
+    cfg = CONFIGS[3].with_(**MLA_SHAPES[shape])
     d = make_inputs(cfg, seed=seed)
     return cfg, {"q": bf16_tensor(d["q"], dev), "kv": bf16_tensor(d["kv"], dev),
                  "bt": torch.from_numpy(d["block_table"]).to(dev),
                  "sl": torch.from_numpy(d["cache_seqlens"]).to(dev)}
 
 
-def test_captured_decode_step_replays_like_eager(dev):
+@pytest.mark.parametrize("shape", list(MLA_SHAPES))
+def test_captured_decode_step_replays_like_eager(dev, shape):
     import torch
     import mla_paged_kv_03_amd as lib
-    cfg, live = _mla_inputs(dev, 1)
+    cfg, live = _mla_inputs(dev, 1, shape)
     B, T, H = cfg.batch, cfg.s_q, cfg.h_q
     plan = lib.mla_decode_plan(live["sl"], T, H, 1, 512)
     new_kv = torch.zeros(B, T, 576, dtype=torch.bfloat16, device=dev)
@@ -53,7 +65,7 @@ def test_captured_decode_step_replays_like_eager(dev):
     with torch.cuda.graph(g):
         step()
     for r in range(3):
-        _, fresh = _mla_inputs(dev, 10 + r)
+        _, fresh = _mla_inputs(dev, 10 + r, shape)
         rng = np.random.default_rng(r)
         nk = torch.from_numpy(rng.standard_normal((B, T, 576)).astype(np.float32)).to(dev)
         for k in ("q", "kv", "bt", "sl"):
@@ -68,7 +80,7 @@ def test_captured_decode_step_replays_like_eager(dev):
         live["kv"].copy_(kv0)
         step()
         torch.cuda.synchronize()
-        log(f"[case] graph replay {r}")
+        log(f"[case] graph replay {shape} {r}")
         assert torch.equal(got_kv, live["kv"])
         assert torch.equal(got_out.view(torch.int16), out.view(torch.int16))
         assert torch.equal(got_lse, lse)
@@ -130,3 +142,47 @@ def test_captured_fp8_and_gqla_steps_replay_like_eager(dev):
         for a, b in zip(got, outs):
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_captured_fp8_decode_at_64_rows_replays_like_eager(dev):
+    """FP8 decode with 128 heads: 64 rows per workgroup, pages dequantised by
+    the copy waves; quantise, plan and decode in one captured step."""
+    import torch
+    import mla_paged_kv_03_amd as lib
+    cfg, live = _mla_inputs(dev, 2, "mixed")
+    B, T, H = cfg.batch, cfg.s_q, cfg.h_q
+    plan = lib.mla_decode_plan(live["sl"], T, H, 1, 512)
+    codes, scales = lib.mla_kv_quantize_fp8(live["kv"])
+    out = torch.empty(B, T, H, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, T, H, dtype=torch.float32, device=dev)
+
+    def step():
+        lib._lib.check("mla_decode_plan", lib._lib.lib().mla_decode_plan(
+            lib._ptr(live["sl"]), B, T, H, 1, 512, lib._ptr(plan.sched_metadata),
+            lib._ptr(plan.num_splits), ctypes.byref(plan.info), lib._stream()))
+        lib.mla_kv_quantize_fp8(live["kv"], codes, scales)
+        lib.mla_decode_fp8(live["q"], codes, scales, live["bt"], live["sl"], cfg.scale,
+                           cfg.causal, plan=plan, out=out, lse=lse)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        _, fresh = _mla_inputs(dev, 20 + r, "mixed")
+        for k in ("q", "kv", "bt", "sl"):
+            live[k].copy_(fresh[k])
+        g.replay()
+        torch.cuda.synchronize()
+        got_out, got_lse = out.clone(), lse.clone()
+        _ = torch.randn(1 << 20, device=dev).sum()
+        step()
+        torch.cuda.synchronize()
+        log(f"[case] graph replay (fp8, 64 rows) {r}")
+        assert torch.equal(got_out.view(torch.int16), out.view(torch.int16))
+        assert torch.equal(got_lse, lse)
