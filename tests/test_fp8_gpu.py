@@ -118,6 +118,8 @@ SMALL = {
     "h128_t2_causal": _mla(10, 2, 128, RAGGED, True),
     "h16_t3_causal": _mla(10, 3, 16, RAGGED, True),
     "h40_t2_causal": _mla(10, 2, 40, RAGGED, True),
+    # dequantising copy waves with one sequence split over every worker
+    "h128_t1_one_long": _mla(1, 1, 128, (20000,), False),
 }
 
 

@@ -258,6 +258,36 @@ def test_attn_combine_matches_oracle_combine(dev):
         check(out[b], lse[b], ro, rl, f"combine b={b}")
 
 
+
+def test_attn_combine_many_partials(dev):
+    """More partials per row than a wave has lanes (100 and 70): the weights
+    of partials 64 and up are recomputed rather than shuffled; some parts see
+    no key, and one row sees none in any part."""
+    import torch
+    import oracle
+    import mla_paged_kv_03_amd as lib
+    rng = np.random.default_rng(8)
+    B, R, dv = 2, 3, 512
+    counts = [100, 70]
+    slots = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    S = int(slots[-1])
+    po = rng.standard_normal((S, R, dv)).astype(np.float32)
+    pl = (rng.standard_normal((S, R)) * 4).astype(np.float32)
+    pl[[5, 64, 99], 1] = -np.inf
+    pl[100:, 2] = -np.inf
+    po[100:, 2] = 0.0
+    out, lse = lib.attn_combine(torch.from_numpy(po).to(dev), torch.from_numpy(pl).to(dev),
+                                torch.from_numpy(slots).to(dev))
+    torch.cuda.synchronize()
+    out = out.float().cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    for b in range(B):
+        parts = [(po[s].astype(np.float64), pl[s].astype(np.float64))
+                 for s in range(slots[b], slots[b + 1])]
+        ro, rl = oracle.combine(parts)
+        check(out[b], lse[b], ro, rl, f"combine many b={b}")
+    assert (out[1, 2] == 0).all() and lse[1, 2] == -np.inf
+
 def _climbing_scores(d, cfg, period=5, step=18.0, seed=7):
     """Give every query head the same q, and page j keys close to
     alpha_j * q with alpha_j chosen so the log2-domain score of page j is
