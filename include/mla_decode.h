@@ -215,8 +215,8 @@ int gqa_kv_append(const void* new_k, const void* new_v, void* k_cache, void* v_c
 /* MLA decode over an FP8 latent cache: as mla_decode, with V = the first
  * 512 dequantised columns. The plan comes from mla_decode_plan with h_kv = 1
  * and head_dim_v = 512. The scales are expected to be powers of two (as
- * mla_kv_quantize_fp8 writes them): at 64 or more query rows per KV head
- * the pages are dequantised to bf16 values code * scale before the
+ * mla_kv_quantize_fp8 writes them): with more than 32 query rows (s_q *
+ * h_q) the pages are dequantised to bf16 values code * scale before the
  * products, which is exact for such scales (any other scale is rounded to
  * bf16 there). Errors as for mla_decode, plus MLA_ERR_NULL_ARG for
  * kv_scales = NULL and MLA_ERR_BAD_SHAPE for a misaligned kv_scales. */
