@@ -173,6 +173,25 @@ def test_fp8_scores_climbing_from_page_to_page(dev, period, heads):
     check(out, lse, ref_out, ref_lse, f"fp8 climbing scores (period {period}, {heads} heads)")
 
 
+@pytest.mark.parametrize("heads", [16, 64])
+def test_fp8_decode_rows_of_every_magnitude(dev, heads):
+    """Cache rows scaled by 2^e, e from -40 to 0 (token scales from about
+    2^-47 to 2^-7): the dequantised values stay exact on both page paths
+    (converted in the compute waves at 16 heads, dequantised by the copy
+    waves at 64), so the decode meets the bars against the oracle."""
+    cfg = _mla(6, 1, heads, (64, 200, 640, 1000, 65, 3), False)
+    d = make_inputs(cfg, seed=21)
+    rng = np.random.default_rng(21)
+    f = (d["kv"].astype(np.uint32) << 16).view(np.float32)
+    e = rng.integers(-40, 1, size=f.shape[:2]).astype(np.float32)
+    d["kv"] = f32_to_bf16_bits(f * np.exp2(e)[:, :, None, None])  # exact in bf16
+    codes, scales = fp8.quantize_cache(d["kv"])
+    log(f"[case] fp8 rows of every magnitude, {heads} heads")
+    out, lse = _decode(d, codes, scales, dev)
+    ref_out, ref_lse = _oracle(d, codes, scales)
+    check(out, lse, ref_out, ref_lse, f"fp8 rows of every magnitude ({heads} heads)")
+
+
 def _sample(cfg, L, k=4):
     rng = np.random.default_rng(99)
     pick = {int(np.argmin(L)), int(np.argmax(L))}
