@@ -20,7 +20,9 @@ not change the time).
     python -m mla_paged_kv_03_amd.path_study [--quick] [--out FILE]
 
 prints one JSON line per measured point and, with --out, writes a Markdown
-table of the step times and the winner per shape.
+table of the step times and the winner per shape. With --long-context it
+times small batches of long sequences instead (step, decode kernel and the
+rest: plan and split merge).
 """
 from __future__ import annotations
 
@@ -76,15 +78,16 @@ def _kernel_time(L, step, K=30):
     return float(np.mean(ms)) * 1e3
 
 
-def measure(kind, h_q, s_q, h_kv, seqlen):
-    """Time one path on one shape; returns a dict of the point."""
+def measure(kind, h_q, s_q, h_kv, seqlen, batch=None):
+    """Time one path on one shape (batch: default about 2^18 cached tokens);
+    returns a dict of the point."""
     import torch
     import mla_paged_kv_03_amd as lib
     from mla_paged_kv_03_amd import _lib
 
     L = _lib.lib()
     dev = torch.device("cuda:0")
-    B = max(1, TOKENS // seqlen)
+    B = batch if batch else max(1, TOKENS // seqlen)
     pages = (seqlen + 63) // 64
     P = B * pages
     g = torch.Generator(device=dev)
@@ -133,15 +136,29 @@ def measure(kind, h_q, s_q, h_kv, seqlen):
     roof_us = max(nbytes / HBM_PEAK, flops / MFMA_PEAK) * 1e6
     return {"path": kind, "h_q": h_q, "s_q": s_q, "h_kv": G, "L": seqlen, "batch": B,
             "step_us": round(step_us, 2), "kernel_us": round(kernel_us, 2),
+            "outside_kernel_us": round(step_us - kernel_us, 2),
             "bytes": nbytes, "flops": flops, "flop_per_byte": round(flops / nbytes, 1),
             "roofline_us": round(roof_us, 2), "frac": round(roof_us / kernel_us, 3)}
+
+
+# small batches of long sequences: a sequence spreads over many workers and
+# its partial results are merged in two launches (path, h_q, s_q, h_kv, L, batch)
+LONG_CONTEXT = [("absorb", 128, 1, 1, 65536, 1), ("absorb", 128, 1, 1, 16384, 1),
+                ("absorb", 16, 1, 1, 131072, 1), ("absorb", 128, 2, 1, 32768, 2),
+                ("gqa", 128, 1, 8, 65536, 1), ("absorb", 128, 1, 1, 4096, 64)]
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--quick", action="store_true", help="a small grid")
+    ap.add_argument("--long-context", action="store_true",
+                    help="time the small-batch long-context shapes instead of the grid")
     ap.add_argument("--out", default=None, help="write a Markdown summary here")
     args = ap.parse_args(argv)
+    if args.long_context:
+        for kind, h, t, g, seqlen, b in LONG_CONTEXT:
+            print(json.dumps(measure(kind, h, t, g, seqlen, batch=b)), flush=True)
+        return 0
     heads = (32, 128) if args.quick else (16, 32, 64, 128)
     tokens = (1, 2) if args.quick else (1, 2, 4)
     groups = (8,) if args.quick else (4, 8, 16)
