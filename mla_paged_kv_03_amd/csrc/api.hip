@@ -167,10 +167,12 @@ int run_decode(int B, int T, int H, int G, int DV, int kind, const void* q, cons
     c.out = a.out;
     c.lse = lse;
     c.B = g.B; c.R = g.TH; c.DV = g.DV;
-    // Sequences of equal length would each reach about W / B + 2 workers;
-    // from 16 partials on, merge in chunks of about 8 (two launches)
+    // Sequences of equal length would each reach about W / B + 2 workers:
+    // from 16 partials on the merge keeps four rows in flight per wave,
+    // from 48 on it merges chunks of about 8 first (two launches)
     const int est = g.W / g.B + 2;
-    c.Z = est >= 16 ? std::min((est + 7) / 8, 32) : 1;
+    c.Z = est >= 48 ? std::min((est + 7) / 8, 32) : 1;
+    c.wide = est >= 16;
     c.level = 0;
     c.chunk_o = a.part_o;
     c.chunk_lse = a.part_lse;
@@ -276,6 +278,7 @@ int attn_combine(const float* o_partial, const float* lse_partial, const int32_t
   c.B = batch; c.R = rows_per_batch; c.DV = dv;
   c.level = 0;  // one pass: the caller's partials are never overwritten
   c.Z = 1;
+  c.wide = 0;
   c.chunk_o = nullptr;
   c.chunk_lse = nullptr;
   return mla::launch_combine_kernel(c, stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;

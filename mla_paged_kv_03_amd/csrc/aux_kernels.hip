@@ -106,9 +106,9 @@ hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int32_t* met
 // workgroup; grid (ceil(R / 4), B, Z). Lane i holds item i's lse (the max
 // and sum are wave reductions); lane l owns columns 4l + 256k, k < NK. The
 // first two items' rows load with the lse values, later ones U at a time,
-// so independent loads are in flight together: two in the one-pass merge,
-// which keeps the registers low enough for eight waves per SIMD, four in
-// the two-launch merge of many partials.
+// so independent loads are in flight together: two in the one-pass merge
+// of a few partials, which keeps the registers low enough for eight waves
+// per SIMD, four where there are many.
 //
 // Items: level 0 merges every partial of the sequence. A sequence spread
 // over many workgroups (one long sequence in a small batch) has up to one
@@ -247,7 +247,10 @@ static void launch_combine_nk(CombineArgs a, hipStream_t st) {
   const unsigned gx = (a.R + COMBINE_ROWS - 1) / COMBINE_ROWS;
   if (a.Z <= 1) {
     a.level = 0;
-    hipLaunchKernelGGL((combine_kernel<NK, 2>), dim3(gx, a.B), block, 0, st, a);
+    if (a.wide)
+      hipLaunchKernelGGL((combine_kernel<NK, 4>), dim3(gx, a.B), block, 0, st, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<NK, 2>), dim3(gx, a.B), block, 0, st, a);
     return;
   }
   a.level = 1;

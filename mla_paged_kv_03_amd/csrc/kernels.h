@@ -47,6 +47,7 @@ struct CombineArgs {
   // into the chunk's first slot of chunk_o / chunk_lse (the same buffers as
   // part_o / part_lse), level 2 merges the chunks' results into out / lse.
   int level, Z;
+  int wide;  // one pass with four partial rows in flight instead of two
   float* chunk_o;
   float* chunk_lse;
 };
