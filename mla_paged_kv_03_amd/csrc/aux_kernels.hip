@@ -152,7 +152,7 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
       n = (ns + c - 1) / c;
     }
   }
-  const bool final = a.level != 1;
+  const bool to_out = a.level != 1;  // else a chunk result
   const size_t row = (size_t)(s0 + first) * a.R + rho;
   const float* po = a.part_o + row * a.DV;
   const float* pl = a.part_lse + row;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
   mx = wave_max64(mx);
   if (mx == -INFINITY) {
     // no key at all: out = 0, lse = -inf (also as a chunk's result)
-    if (final) {
+    if (to_out) {
       uint16_t* orow = a.out + ((size_t)b * a.R + rho) * a.DV;
       for (int c = lane * 4; c < a.DV; c += 64 * 4) *(u32x2*)(orow + c) = u32x2{0u, 0u};
       if (lane == 0) a.lse[(size_t)b * a.R + rho] = -INFINITY;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
       for (int u = 0; u < U; ++u) acc[k] += w[u] * x[u][k];
   }
   const float lse_v = mx + __logf(tot);
-  if (final) {
+  if (to_out) {
     uint16_t* orow = a.out + ((size_t)b * a.R + rho) * a.DV;
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
