@@ -96,6 +96,18 @@ typedef struct {
  * nothing is enqueued, so callers can size buffers first. The sizes depend
  * only on the shape arguments and the current device. The plan may be
  * reused by every layer of the step (same cache_seqlens and shape).
+ *
+ * sched_metadata opens with 8 int32 words that record the geometry the plan
+ * was made for: a fixed tag 0x4D4C4150, the worker count, batch, s_q * h_q,
+ * h_kv and head_dim_v (then two zero words). The decode kernels and their
+ * internal merge compare this signature with their own call before they
+ * read any worker record or slot; on a mismatch (a plan made for another
+ * batch, s_q * h_q, h_kv, value width or device) they return at once and
+ * leave out and lse unwritten. The call itself still returns MLA_OK: the
+ * check runs on the device. A plan made for the same shape but other
+ * cache_seqlens (a stale plan) gives undefined results, but every page range
+ * is clamped to the current lengths, so no block-table entry or page slot
+ * outside what the current lengths reach is read.
  */
 int mla_decode_plan(const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
                     int32_t h_q, int32_t h_kv, int32_t head_dim_v,

@@ -80,7 +80,7 @@ int make_geom(int B, int T, int H, int G, int DV, int cus, Geom* g) {
   g->W = W;
   g->TH = T * H;
   g->max_slots = 2 * (W - 1);
-  g->meta_bytes = ((size_t)W * sched::REC + (size_t)B + 1) * sizeof(int32_t);
+  g->meta_bytes = ((size_t)sched::HDR + (size_t)W * sched::REC + (size_t)B + 1) * sizeof(int32_t);
   g->split_bytes = ((size_t)B + 1) * sizeof(int32_t);
   const size_t o_bytes = (size_t)g->max_slots * g->TH * DV * sizeof(float);
   const size_t l_bytes = (size_t)g->max_slots * g->TH * sizeof(float);
@@ -161,6 +161,7 @@ int run_decode(int B, int T, int H, int G, int DV, int kind, const void* q, cons
   if (g_prof_stop && hipEventRecord(g_prof_stop, st) != hipSuccess) return MLA_ERR_HIP;
   if (g.max_slots > 0) {
     mla::CombineArgs c;
+    c.meta = meta;
     c.part_o = a.part_o;
     c.part_lse = a.part_lse;
     c.slots = splits;
@@ -234,8 +235,8 @@ int mla_decode_plan(const int32_t* cache_seqlens, int32_t batch, int32_t s_q, in
   make_geom(batch, s_q, h_q, h_kv, head_dim_v, cus, &g);
   fill_info(g, info);
   if (!sched_metadata && !num_splits) return MLA_OK;
-  if (mla::launch_plan_kernel(cache_seqlens, batch, g.W, sched_metadata, num_splits, stream) !=
-      hipSuccess)
+  if (mla::launch_plan_kernel(cache_seqlens, batch, g.W, g.TH, g.G, g.DV, sched_metadata,
+                              num_splits, stream) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
 }
@@ -270,6 +271,7 @@ int attn_combine(const float* o_partial, const float* lse_partial, const int32_t
   if (!o_partial || !lse_partial || !num_splits || !out || !lse) return MLA_ERR_NULL_ARG;
   if (!aligned16(o_partial) || !aligned16(out)) return MLA_ERR_BAD_SHAPE;
   mla::CombineArgs c;
+  c.meta = nullptr;  // the caller's own slot prefix: no plan to check
   c.part_o = o_partial;
   c.part_lse = lse_partial;
   c.slots = num_splits;
@@ -449,12 +451,13 @@ int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q
   if (!sched_metadata_host && !num_splits_host) return MLA_OK;
   if (!sched_metadata_host || !num_splits_host || (batch > 0 && !seqlens_host))
     return MLA_ERR_NULL_ARG;
-  int32_t* prefix = sched_metadata_host + (size_t)g.W * sched::REC;
+  sched::write_header(sched_metadata_host, g.W, batch, g.TH, g.G, g.DV);
+  int32_t* prefix = sched::unit_prefix(sched_metadata_host, g.W);
   prefix[0] = 0;
   for (int b = 0; b < batch; ++b) prefix[b + 1] = prefix[b] + sched::seq_units(seqlens_host[b]);
   for (int w = 0; w < g.W; ++w)
     sched::worker_record(w, g.W, prefix, seqlens_host, batch,
-                         sched_metadata_host + (size_t)w * sched::REC);
+                         sched::records(sched_metadata_host) + (size_t)w * sched::REC);
   int32_t acc = 0;
   for (int b = 0; b < batch; ++b) {
     num_splits_host[b] = acc;

@@ -45,20 +45,22 @@ __device__ int block_scan(int v, int* wsum, int* total) {
 // global memory.
 constexpr int PLAN_LDS_SEQS = 8192;
 
-// One workgroup. Writes the unit prefix (B + 1 entries after the W worker
-// records), every worker record, and the exclusive prefix of partial slots
-// (B + 1 entries).
+// One workgroup. Writes the plan's signature, the unit prefix (B + 1 entries
+// after the W worker records), every worker record, and the exclusive prefix
+// of partial slots (B + 1 entries).
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqlens, int B, int W,
+                                                           int rows, int G, int DV,
                                                            int32_t* meta, int32_t* slots) {
   __shared__ int buf[PLAN_WAVES];
   __shared__ int32_t s_prefix[PLAN_LDS_SEQS + 1];
   __shared__ int32_t s_len[PLAN_LDS_SEQS];
   const int tid = threadIdx.x;
-  int32_t* prefix = meta + (size_t)W * sched::REC;
+  int32_t* prefix = sched::unit_prefix(meta, W);
   const bool in_lds = B <= PLAN_LDS_SEQS;
 
   int carry = 0, total = 0;
   if (tid == 0) {
+    sched::write_header(meta, W, B, rows, G, DV);
     prefix[0] = 0;
     s_prefix[0] = 0;
   }
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
   const int32_t* len = in_lds ? s_len : seqlens;
 
   for (int w = tid; w < W; w += PLAN_THREADS)
-    sched::worker_record(w, W, pre, len, B, meta + (size_t)w * sched::REC);
+    sched::worker_record(w, W, pre, len, B, sched::records(meta) + (size_t)w * sched::REC);
 
   carry = 0;
   for (int base = 0; base < B; base += PLAN_THREADS) {
@@ -95,9 +97,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
   if (tid == 0) slots[B] = carry;
 }
 
-hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int32_t* meta,
-                              int32_t* slots, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, seqlens, B, W, meta, slots);
+hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int rows, int G, int DV,
+                              int32_t* meta, int32_t* slots, hipStream_t st) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, seqlens, B, W, rows, G, DV,
+                     meta, slots);
   return hipGetLastError();
 }
 
@@ -136,6 +139,11 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
   const int rho = blockIdx.x * COMBINE_ROWS + (threadIdx.x >> 6);
   const int b = blockIdx.y;
   if (rho >= a.R) return;
+  // inside a decode call: the slot prefix must come from a plan made for
+  // this batch and row shape (else the slots may lie past the workspace)
+  if (a.meta && (a.meta[sched::H_MAGIC] != sched::PLAN_MAGIC || a.meta[sched::H_B] != a.B ||
+                 a.meta[sched::H_ROWS] != a.R || a.meta[sched::H_DV] != a.DV))
+    return;
   const int s0 = a.slots[b];
   const int ns = a.slots[b + 1] - s0;
   if (ns <= 0) return;

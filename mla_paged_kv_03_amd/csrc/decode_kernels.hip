@@ -98,7 +98,14 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
   const int g = rb / a.nrb;
   const int rblk = rb - g * a.nrb;
 
-  const int32_t* rec = a.meta + w * sched::REC;
+  // a plan made for another geometry: leave every output untouched rather
+  // than index records or slots that belong to a different layout
+  const int32_t* hdr = a.meta;
+  if (hdr[sched::H_MAGIC] != sched::PLAN_MAGIC || hdr[sched::H_W] != a.W ||
+      hdr[sched::H_B] != a.B || hdr[sched::H_ROWS] != a.T * a.H || hdr[sched::H_G] != a.G ||
+      hdr[sched::H_DV] != LY::DV)
+    return;
+  const int32_t* rec = sched::records(a.meta) + w * sched::REC;
   const int bs = uniform(rec[sched::R_B_START]);
   const int be = uniform(rec[sched::R_B_END]);
   if (be < bs) return;
@@ -177,8 +184,10 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
   for (int b = bs; b <= be; ++b) {
     const int L = uniform(a.seqlens[b]);
     const int npg = sched::seq_pages(L);
-    const int p0 = uniform(b == bs ? rec[sched::R_P_START] : 0);
-    const int p1 = uniform(b == be ? rec[sched::R_P_END] : npg);
+    int p0, p1;
+    sched::page_range(rec, b, bs, be, npg, &p0, &p1);
+    p0 = uniform(p0);
+    p1 = uniform(p1);
     const int s0 = uniform(a.slots[b]);
     const int nslots = uniform(a.slots[b + 1]) - s0;
 

@@ -21,7 +21,7 @@ struct DecodeArgs {
   const float* kscale;         // [P, 64] per-token scales of an FP8 cache, else null
   const int32_t* block_table;  // [B, bt_stride]
   const int32_t* seqlens;      // [B]
-  const int32_t* meta;         // worker records [W][REC], then unit prefix [B + 1]
+  const int32_t* meta;         // signature [HDR], worker records [W][REC], unit prefix [B + 1]
   const int32_t* slots;        // [B + 1] partial slots per sequence
   float* part_o;               // [slots][T*H][DV]
   float* part_lse;             // [slots][T*H]
@@ -36,6 +36,7 @@ struct DecodeArgs {
 };
 
 struct CombineArgs {
+  const int32_t* meta;         // the plan's metadata (its signature is checked), or null
   const float* part_o;         // [slots][R][DV]
   const float* part_lse;       // [slots][R]
   const int32_t* slots;        // [B + 1]
@@ -121,8 +122,9 @@ hipError_t launch_combine_kernel(const CombineArgs& a, hipStream_t st);
 // Device-side precondition check of the decode calls (one workgroup).
 hipError_t launch_check_pages(const int32_t* block_table, const int32_t* seqlens, int B,
                               int num_pages, int max_pages, int32_t* status, hipStream_t st);
-// Schedule: worker records and unit prefix into meta, slot prefix into slots.
-hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int32_t* meta,
-                              int32_t* slots, hipStream_t st);
+// Schedule: signature, worker records and unit prefix into meta, slot
+// prefix into slots.
+hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int rows, int G, int DV,
+                              int32_t* meta, int32_t* slots, hipStream_t st);
 
 }  // namespace mla

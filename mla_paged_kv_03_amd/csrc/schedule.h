@@ -28,6 +28,32 @@ constexpr int PAGE = 64;
 constexpr int FIXED_UNITS = 2;
 constexpr int REC = 8;  // int32 per worker record
 
+// The metadata opens with a signature of the geometry the plan was made for
+// (HDR int32 words); the worker records follow it, then the unit prefix.
+// The decode and merge kernels compare it with their own geometry before
+// they index any record or slot, and leave every output untouched when a
+// plan made for another batch, worker count, row count, KV head count or
+// value width is passed in.
+constexpr int HDR = 8;
+constexpr int32_t PLAN_MAGIC = 0x4D4C4150;  // "PALM" in memory order
+enum : int { H_MAGIC = 0, H_W = 1, H_B = 2, H_ROWS = 3, H_G = 4, H_DV = 5 };
+
+SCHED_HD void write_header(int32_t* hdr, int W, int B, int rows, int G, int DV) {
+  hdr[H_MAGIC] = PLAN_MAGIC;
+  hdr[H_W] = W;
+  hdr[H_B] = B;
+  hdr[H_ROWS] = rows;
+  hdr[H_G] = G;
+  hdr[H_DV] = DV;
+  hdr[6] = 0;
+  hdr[7] = 0;
+}
+
+// Records of the workers, and the unit prefix, inside the metadata.
+SCHED_HD const int32_t* records(const int32_t* meta) { return meta + HDR; }
+SCHED_HD int32_t* records(int32_t* meta) { return meta + HDR; }
+SCHED_HD int32_t* unit_prefix(int32_t* meta, int W) { return meta + HDR + (size_t)W * REC; }
+
 // Worker record layout (int32 x REC).
 enum : int {
   R_B_START = 0,    // first sequence touched
@@ -88,6 +114,20 @@ SCHED_HD void worker_record(int w, int W, const int32_t* prefix, const int32_t* 
   rec[R_OWNS_FIRST] = prefix[bs] == lo ? 1 : 0;
   rec[R_LO] = (int32_t)lo;
   rec[R_HI] = (int32_t)hi;
+}
+
+// Pages [p0, p1) of sequence b (with npg pages) that worker record rec
+// covers, given the worker's first and last sequences bs and be. Clamped to
+// the sequence's current page count, so a plan made for longer lengths never
+// sends a worker past the pages the lengths reach (the result is then not
+// the attention of those lengths, but nothing outside them is read).
+SCHED_HD void page_range(const int32_t* rec, int b, int bs, int be, int npg, int* p0, int* p1) {
+  int lo = b == bs ? rec[R_P_START] : 0;
+  int hi = b == be ? rec[R_P_END] : npg;
+  hi = hi < npg ? hi : npg;
+  lo = lo < 0 ? 0 : lo;
+  *p0 = lo;
+  *p1 = hi;
 }
 
 // Number of workers that process pages of sequence b (1 for an empty one).

@@ -200,6 +200,79 @@ def test_softmax_rows_sum_to_one():
                 assert (w >= 0).all()
 
 
+def test_softmax_weights_match_worked_examples():
+    # hand-worked weights: equal scores, one key, scores 0 and 1, and the
+    # bottom-right causal case (token 0 of two sees only key 0)
+    with open(os.path.join(HERE, "golden", "worked_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        q, kv, bt, L = _golden_inputs(case)
+        for t, per_head in enumerate(case["weights"]):
+            w = softmax_weights(q, kv, bt, L, case["scale"], case["causal"], 0, t)
+            np.testing.assert_allclose(w, np.array(per_head), rtol=1e-14, atol=1e-15,
+                                       err_msg=f"{case['name']} token {t}")
+
+
+@pytest.mark.parametrize("name", ["mla_causal2", "mla_causal3", "gqa", "gqa_causal"])
+def test_softmax_weights_reproduce_bruteforce(name):
+    """The weights of every (b, t, h) times the V rows of the visible keys
+    give the dense brute-force output, and a row with no visible key has no
+    weights exactly where brute force gives lse = -inf. A wrong scale, head
+    to group map or visible count in the weights moves the product."""
+    d = tiny(name)
+    cfg = d["cfg"]
+    ob, lb = run(attend_bruteforce, d)
+    hpg = cfg.h_q // cfg.h_kv
+    vcache = d["kv"] if cfg.kind == "mla" else d["v"]
+    for b in range(cfg.batch):
+        for t in range(cfg.s_q):
+            w = softmax_weights(d["q"], d["kv" if cfg.kind == "mla" else "k"],
+                                d["block_table"], d["cache_seqlens"], cfg.scale, cfg.causal,
+                                b, t)
+            vis = w.shape[1]
+            if vis == 0:
+                assert (lb[b, t] == -np.inf).all()
+                continue
+            # V rows of keys 0 .. vis-1, slot by slot (no page walk)
+            V = np.stack([bf16_to_f64(vcache[d["block_table"][b, j // 64], j % 64])
+                          for j in range(vis)])[..., :cfg.d_v]        # [vis, G, dv]
+            for h in range(cfg.h_q):
+                np.testing.assert_allclose(w[h] @ V[:, h // hpg], ob[b, t, h], rtol=1e-12,
+                                           atol=1e-12, err_msg=f"{name} b={b} t={t} h={h}")
+
+
+def _weights_pins_hold():
+    """True when the two pins above hold for the current softmax_weights."""
+    try:
+        test_softmax_weights_match_worked_examples()
+        for name in ("mla_causal2", "gqa", "gqa_causal"):
+            test_softmax_weights_reproduce_bruteforce(name)
+    except (AssertionError, IndexError, ValueError):
+        return False
+    return True
+
+
+@pytest.mark.parametrize("plant", ["scale dropped", "strided group map", "top-left causal",
+                                   "one key short"])
+def test_softmax_weights_pins_catch_planted_mistakes(monkeypatch, plant):
+    """Each plausible mistake in the weights fails one of the pins above."""
+    import oracle.attention as A
+    assert _weights_pins_hold()
+    if plant == "scale dropped":
+        monkeypatch.setattr(A, "scale_as_received", lambda s: 1.0)
+    elif plant == "strided group map":
+        monkeypatch.setattr(A, "_heads_per_group", lambda H, G: 1)
+    elif plant == "top-left causal":
+        monkeypatch.setattr(A, "visible_keys",
+                            lambda L, s_q, t, causal: min(t + 1, L) if causal else L)
+    else:
+        monkeypatch.setattr(A, "visible_keys", lambda L, s_q, t, causal: max(
+            (min(L - s_q + 1 + t, L) if causal else L) - 1, 0))
+    held = _weights_pins_hold()
+    monkeypatch.undo()
+    assert not held, f"planted mistake not caught: {plant}"
+
+
 def test_constant_v_gives_that_constant():
     # with every V entry equal to c, out = c * (sum of weights) = c
     d = tiny("gqa")
