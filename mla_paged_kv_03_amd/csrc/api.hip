@@ -162,6 +162,8 @@ int run_decode(int B, int T, int H, int G, int DV, int kind, const void* q, cons
   if (g.max_slots > 0) {
     mla::CombineArgs c;
     c.meta = meta;
+    c.W = g.W;
+    c.G = g.G;
     c.part_o = a.part_o;
     c.part_lse = a.part_lse;
     c.slots = splits;
@@ -272,6 +274,8 @@ int attn_combine(const float* o_partial, const float* lse_partial, const int32_t
   if (!aligned16(o_partial) || !aligned16(out)) return MLA_ERR_BAD_SHAPE;
   mla::CombineArgs c;
   c.meta = nullptr;  // the caller's own slot prefix: no plan to check
+  c.W = 0;
+  c.G = 0;
   c.part_o = o_partial;
   c.part_lse = lse_partial;
   c.slots = num_splits;

@@ -140,9 +140,11 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
   const int b = blockIdx.y;
   if (rho >= a.R) return;
   // inside a decode call: the slot prefix must come from a plan made for
-  // this batch and row shape (else the slots may lie past the workspace)
-  if (a.meta && (a.meta[sched::H_MAGIC] != sched::PLAN_MAGIC || a.meta[sched::H_B] != a.B ||
-                 a.meta[sched::H_ROWS] != a.R || a.meta[sched::H_DV] != a.DV))
+  // this call's geometry, the one the decode kernel checked (else the
+  // slots may lie past the workspace, or hold no partials of this call)
+  if (a.meta && (a.meta[sched::H_MAGIC] != sched::PLAN_MAGIC || a.meta[sched::H_W] != a.W ||
+                 a.meta[sched::H_B] != a.B || a.meta[sched::H_ROWS] != a.R ||
+                 a.meta[sched::H_G] != a.G || a.meta[sched::H_DV] != a.DV))
     return;
   const int s0 = a.slots[b];
   const int ns = a.slots[b + 1] - s0;

@@ -37,6 +37,7 @@ struct DecodeArgs {
 
 struct CombineArgs {
   const int32_t* meta;         // the plan's metadata (its signature is checked), or null
+  int W, G;                    // workers and KV heads of the decode call (with meta)
   const float* part_o;         // [slots][R][DV]
   const float* part_lse;       // [slots][R]
   const int32_t* slots;        // [B + 1]
