@@ -350,6 +350,121 @@ def bench_gqla(args):
                       "algorithmic_bytes": exp_bytes, "flops": exp_flops}}), flush=True)
 
 
+def bench_ceilings(args):
+    """Practical ceilings measured with the decode's own instructions, next to
+    the nominal peaks: bf16 MFMA loops on register operands (16x16x32 and
+    32x32x16, one and two waves per SIMD), a non-temporal streaming read of
+    4 GiB, and the HBM -> LDS page-copy loop of the decode alone (2 GiB in
+    72 KiB blocks, one workgroup per CU), plus torch's bf16 GEMM (hipBLASLt)
+    at 8192^3 for reference. Events around back-to-back launches after a
+    warm-up; one JSON line per measurement."""
+    import torch
+    from mla_paged_kv_03_amd import _lib
+
+    L = _lib.lib()
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda x: ctypes.c_void_p(x.data_ptr())
+    n = max(1, args.steps)
+
+    def timed(fn, reps):
+        for _ in range(max(2, reps // 4)):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps * 1e-3  # seconds per launch
+
+    def emit(name, achieved, unit, peak, extra):
+        rec = {"ceiling": name, "achieved": round(achieved, 1), "unit": unit, "peak": peak,
+               "frac_of_peak": round(achieved / peak, 4)}
+        rec.update(extra)
+        print(json.dumps(rec), flush=True)
+
+    which = args.ceiling
+    if which in ("mfma", "all"):
+        sink = torch.empty(cus * 2 * 256, dtype=torch.float32, device=dev)
+        iters = 4096
+        for kind, nacc, name in ((0, 4, "16x16x32"), (0, 8, "16x16x32"), (1, 2, "32x32x16"),
+                                 (1, 4, "32x32x16")):
+            for wps in (1, 2):
+                def call():
+                    rc = L.mla_ceiling_mfma(kind, nacc, wps, iters, cus, P(sink), stream)
+                    if rc:
+                        raise RuntimeError(f"mla_ceiling_mfma failed with {rc}")
+                sec = timed(call, n)
+                # per wave: iters * nacc MFMAs; 4 waves per workgroup
+                flop = (16384 if kind == 0 else 32768) * nacc * iters * cus * wps * 4
+                emit(f"mfma_bf16_{name}", flop / sec / 1e12, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS,
+                     {"accumulators": nacc, "waves_per_simd": wps, "launch_us": round(sec * 1e6, 1)})
+    if which in ("stream", "all"):
+        nbytes = 4 << 30
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        sink = torch.empty(cus * 8 * 256, dtype=torch.int32, device=dev)
+        for per_cu in (4, 8):
+            def call():
+                rc = L.mla_ceiling_stream_read(P(buf), nbytes, cus * per_cu, P(sink), stream)
+                if rc:
+                    raise RuntimeError(f"mla_ceiling_stream_read failed with {rc}")
+            sec = timed(call, max(3, n // 10))
+            emit("hbm_stream_read", nbytes / sec / 1e9, "GB/s", HBM_PEAK_GBS,
+                 {"bytes": nbytes, "workgroups_per_cu": per_cu, "launch_us": round(sec * 1e6, 1)})
+        del buf
+    if which in ("lds", "all"):
+        blk = 72 * 1024
+        nblocks = (2 << 30) // blk
+        nbytes = nblocks * blk
+        buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        sink = torch.empty(cus, dtype=torch.int32, device=dev)
+        for waves in (4, 8):
+            def call():
+                rc = L.mla_ceiling_lds_fill(P(buf), nbytes, waves, cus, P(sink), stream)
+                if rc:
+                    raise RuntimeError(f"mla_ceiling_lds_fill failed with {rc}")
+            sec = timed(call, max(3, n // 10))
+            emit("hbm_to_lds_page_copies", nbytes / sec / 1e9, "GB/s", HBM_PEAK_GBS,
+                 {"bytes": nbytes, "waves": waves, "workgroups": cus,
+                  "per_cu_bytes_per_clk_at_2.4GHz": round(nbytes / sec / cus / 2.4e9, 2),
+                  "launch_us": round(sec * 1e6, 1)})
+        del buf
+    if which in ("ldsop", "all"):
+        iters = 2048
+        sink = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+        for mode, name in ((0, "ds_read_b128"), (1, "ds_read_b128+mfma32"),
+                           (3, "ds_read_b64_tr_x2"), (2, "ds_read_b64_tr_x2+mfma32"),
+                           (4, "ds_read_b128+mfma32_prefetch8"),
+                           (5, "ds_read_b64_tr_x2+mfma32_prefetch8")):
+            for waves in (4, 8):
+                def call():
+                    rc = L.mla_ceiling_lds_operand(mode, waves, iters, cus, P(sink), stream)
+                    if rc:
+                        raise RuntimeError(f"mla_ceiling_lds_operand failed with {rc}")
+                sec = timed(call, n)
+                steps = iters * 16 * waves * cus          # one KiB and (modes 1, 2) one MFMA each
+                extra = {"waves": waves, "lds_bytes_per_clk_per_cu_at_2.4GHz":
+                         round(steps * 1024 / sec / cus / 2.4e9, 1), "launch_us": round(sec * 1e6, 1)}
+                if mode in (1, 2, 4, 5):
+                    emit(f"lds_operand_{name}", steps * 32768 / sec / 1e12, "TFLOP/s",
+                         MFMA_BF16_PEAK_TFLOPS, extra)
+                else:
+                    # nominal: 128 bytes per clock per CU at 2.4 GHz
+                    emit(f"lds_operand_{name}", steps * 1024 / sec / 1e9, "GB/s",
+                         round(128 * cus * 2.4, 1), extra)
+    if which in ("gemm", "all"):
+        m = 8192
+        a = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+        b = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
+        c = torch.empty(m, m, dtype=torch.bfloat16, device=dev)
+        sec = timed(lambda: torch.matmul(a, b, out=c), max(5, n // 10))
+        emit("torch_bf16_gemm_8192", 2 * m ** 3 / sec / 1e12, "TFLOP/s", MFMA_BF16_PEAK_TFLOPS,
+             {"launch_us": round(sec * 1e6, 1)})
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +484,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--ceiling", choices=["mfma", "stream", "lds", "ldsop", "gemm", "all"], default=None,
+                    help="only measure practical ceilings: bf16 MFMA loops, a streaming HBM "
+                         "read, the decode's HBM -> LDS page-copy loop alone, LDS operand reads "
+                         "with and without MFMAs, torch's bf16 GEMM")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs the decode on one GPU only; "
@@ -376,6 +495,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.ceiling:
+        bench_ceilings(args)
+        return
     if args.copy_calibration:
         n = 1 << 30
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")

@@ -44,6 +44,10 @@ _SIGS = {
     "mla_decode_plan_host": [_P, _I, _I, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PlanInfo)],
     "mla_check_pages": [_P, _P, _I, _I, _I, _P, _P],
     "mla_status_string": [ctypes.c_int],
+    "mla_ceiling_mfma": [_I, _I, _I, _I, _I, _P, _P],
+    "mla_ceiling_stream_read": [_P, ctypes.c_size_t, _I, _P, _P],
+    "mla_ceiling_lds_fill": [_P, ctypes.c_size_t, _I, _I, _P, _P],
+    "mla_ceiling_lds_operand": [_I, _I, _I, _I, _P, _P],
     "mla_profile_events": [_P, _P],
 }
 
@@ -79,8 +83,12 @@ def check(fn: str, code: int) -> None:
 
 
 def header_functions() -> list[str]:
-    """Names of the functions include/mla_decode.h declares."""
-    with open(HEADER) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    """Names of the functions every header under include/ declares."""
+    import glob
+    names = []
+    for path in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return names

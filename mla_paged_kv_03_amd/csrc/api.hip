@@ -43,6 +43,12 @@ struct Geom {
   int nw;     // row groups of 16 rows per workgroup (1, 2 or 4)
   int nrb;    // row blocks per KV head
   int RB;     // row blocks per worker (all KV heads)
+  // latent cache with 128 or more rows per KV head: the workers are those
+  // of 128-row workgroups; the bf16 decode runs one 128-row block per
+  // workgroup (nrb128 of them per worker), the FP8 decode keeps its 64-row
+  // blocks (nrb of them per worker) over the same workers
+  bool big;
+  int nrb128;
   int W;      // workers
   int TH;
   int max_slots;
@@ -71,10 +77,12 @@ int make_geom(int B, int T, int H, int G, int DV, int cus, Geom* g) {
   const int rows = 16 * g->nw;
   g->nrb = (g->M + rows - 1) / rows;
   g->RB = G * g->nrb;
+  g->big = !g->gqa && g->M >= 128;
+  g->nrb128 = (g->M + 127) / 128;
   // one workgroup per CU for the latent cache (two 72 KiB page buffers);
   // the GQA pages are 32 KiB, so two workgroups share a CU
   const int per_cu = g->gqa ? 2 : 1;
-  int W = cus * per_cu / g->RB;
+  int W = cus * per_cu / (g->big ? g->nrb128 : g->RB);
   if (W >= 8) W -= W % 8;
   if (W < 1) W = 1;
   g->W = W;
@@ -157,7 +165,14 @@ int run_decode(int B, int T, int H, int G, int DV, int kind, const void* q, cons
   a.scale_log2 = scale * 1.4426950408889634f;
   a.causal = causal;
   if (g_prof_start && hipEventRecord(g_prof_start, st) != hipSuccess) return MLA_ERR_HIP;
-  if (mla::launch_decode_kernel(a, g.nw, kind, g.W * g.RB, st) != hipSuccess) return MLA_ERR_HIP;
+  hipError_t e;
+  if (g.big && kind == mla::KIND_MLA) {
+    a.nrb = g.nrb128;
+    e = mla::launch_decode128_kernel(a, g.W * g.nrb128, st);
+  } else {
+    e = mla::launch_decode_kernel(a, g.nw, kind, g.W * g.RB, st);
+  }
+  if (e != hipSuccess) return MLA_ERR_HIP;
   if (g_prof_stop && hipEventRecord(g_prof_stop, st) != hipSuccess) return MLA_ERR_HIP;
   if (g.max_slots > 0) {
     mla::CombineArgs c;

@@ -200,9 +200,12 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
 // Scalar load of one int32 from a wave-uniform address. The wait sits in the
 // same asm statement, so the result is ready when the statement ends; it is
 // a scalar-cache load and does not touch vmcnt, which counts page copies.
+// The block opens with one wait state after a possible VALU write of the
+// address registers (a v_readfirstlane or v_readlane just before it).
 __device__ __forceinline__ int sload(const int32_t* p) {
   int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  asm volatile("s_nop 0\n\ts_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p)
+               : "memory");
   return v;
 }
 

@@ -115,6 +115,9 @@ hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t st);
 // Paged KV append: one wave per new token.
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t st);
 
+// The latent decode at 128 query rows per workgroup (32x32x16 MFMA, four
+// waves of 32 rows): grid = workers * row blocks of 128.
+hipError_t launch_decode128_kernel(const DecodeArgs& a, int grid, hipStream_t st);
 // One decode launch: grid = workers * row blocks, 64 * nw threads.
 hipError_t launch_decode_kernel(const DecodeArgs& a, int nw, int kind, int grid, hipStream_t st);
 // Split-KV merge of the partial results of split sequences (one level, or

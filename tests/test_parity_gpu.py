@@ -43,6 +43,13 @@ SMALL = {
     "mla_h16_t1_one_long": _mla(1, 1, 16, (16384,), False),
     "mla_h128_t2_causal_long": _mla(3, 2, 128, (20000, 3, 700), True),
     "gqa_h16_g2_one_long": _gqa(1, 1, 16, 2, (30000,)),
+    # 4 query tokens at 128 heads: 512 rows in four 128-row blocks
+    "mla_h128_t4_causal": _mla(6, 4, 128, (1, 64, 65, 200, 1000, 3000), True),
+    # 150 rows: the second 128-row block ends inside a wave's 32 rows, whose
+    # output then leaves without the staged row stores
+    "mla_h50_t3_causal": _mla(10, 3, 50, RAGGED, True),
+    # 16 KV heads of 8 query heads each
+    "gqa_h128_g16": _gqa(10, 1, 128, 16, RAGGED),
     "gqa_h128_g8": _gqa(10, 1, 128, 8, RAGGED),
     "gqa_h16_g2": _gqa(10, 1, 16, 2, RAGGED),
     "gqa_h8_g8": _gqa(10, 1, 8, 8, RAGGED),
