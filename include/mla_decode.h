@@ -60,7 +60,8 @@ enum {
   MLA_ERR_BAD_SHAPE = -2,           /* negative size, h_q % h_kv != 0, ... */
   MLA_ERR_UNSUPPORTED = -3,         /* head dims or row counts not built */
   MLA_ERR_WORKSPACE_TOO_SMALL = -4, /* workspace_bytes below the plan's */
-  MLA_ERR_HIP = -5                  /* a HIP runtime call or launch failed */
+  MLA_ERR_HIP = -5,                 /* a HIP runtime call or launch failed */
+  MLA_ERR_SCRATCH_LIMIT = -6        /* mla_decode_noalloc: needs more than its static scratch */
 };
 
 /* Host-side description of a decode plan, filled by mla_decode_plan. */
@@ -137,6 +138,29 @@ int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
                int32_t causal, const int32_t* sched_metadata, const int32_t* num_splits,
                void* workspace, size_t workspace_bytes, void* out, float* lse,
                hipStream_t stream);
+
+/* mla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same plan, decode and merge kernels, with the plan's metadata, its
+ * slot prefix and the split partials in a static device array of the
+ * library (137 MiB per GPU, allocated when the library's code is loaded on
+ * that GPU and held until the process ends) instead of caller buffers.
+ *
+ * Arguments as for mla_decode, without the plan and workspace. The call
+ * enqueues the plan kernel, the decode and (when a sequence is split) the
+ * merge on `stream`, and calls no allocating routine. Limits: 512 KiB of
+ * plan metadata and slot prefix each (batch up to about 128k sequences)
+ * and 136 MiB of partials, which every s_q * h_q fits on a 256-CU GPU;
+ * larger calls return MLA_ERR_SCRATCH_LIMIT before anything is enqueued.
+ * Every call on one GPU uses that GPU's one array, and each call leaves
+ * its contents behind: two calls on one GPU whose work overlaps in time
+ * (on different streams, or from different host threads) race and give
+ * undefined results. Calls in order on one stream are safe.
+ */
+int mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                       const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                       int32_t num_pages, int32_t max_pages_per_seq, float softmax_scale,
+                       int32_t causal, void* out, float* lse, hipStream_t stream);
 
 /* GQA decode with a per-group expanded cache (GQLA review, "1. Key Terms &
  * Definitions", GQA path).

@@ -20,6 +20,7 @@ from . import _lib
 from ._lib import DecodeError, PlanInfo
 
 __all__ = ["Plan", "PlanInfo", "DecodeError", "plan_info", "mla_decode_plan", "mla_decode",
+           "mla_decode_noalloc",
            "gqa_decode", "attn_combine", "mla_kv_append", "gqa_kv_append",
            "mla_decode_fp8", "mla_kv_append_fp8", "mla_kv_quantize_fp8", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output", "gqla_decode",
            "mla_decode_plan_host", "mla_check_pages", "profile_events"]
@@ -125,6 +126,36 @@ def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal=Fa
         kv_cache.shape[0], block_table.shape[1], float(softmax_scale), int(bool(causal)),
         _ptr(plan.sched_metadata), _ptr(plan.num_splits), ws, wsb, _ptr(out), _ptr(lse),
         _stream()))
+    return out, lse
+
+
+def mla_decode_noalloc(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal=False,
+                       out=None, lse=None):
+    """mla_decode without plan or workspace buffers: the library plans into
+    its own static device scratch (see include/mla_decode.h). Calls on one
+    GPU share that scratch, so they must not overlap in time. With out and
+    lse given, nothing is allocated on the way."""
+    _need(q, "q", torch.bfloat16, 4)
+    _need(kv_cache, "kv_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
+    B, T, H, D = q.shape
+    if D != MLA_D or tuple(kv_cache.shape[1:]) != (64, 1, MLA_D):
+        raise ValueError("mla_decode_noalloc expects q [..., 576] and kv_cache [P, 64, 1, 576]")
+    if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
+        raise ValueError("batch mismatch")
+    if out is None:
+        out = torch.empty(B, T, H, MLA_DV, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, T, H, dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.bfloat16)
+    _need(lse, "lse", torch.float32)
+    if tuple(out.shape) != (B, T, H, MLA_DV) or tuple(lse.shape) != (B, T, H):
+        raise ValueError("out must be [B, s_q, h_q, 512] and lse [B, s_q, h_q]")
+    _lib.check("mla_decode_noalloc", _lib.lib().mla_decode_noalloc(
+        _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens), B, T, H,
+        kv_cache.shape[0], block_table.shape[1], float(softmax_scale), int(bool(causal)),
+        _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

@@ -11,7 +11,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "mla_decode.h")
 
 MLA_OK = 0
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL_ARG", -2: "MLA_ERR_BAD_SHAPE",
-          -3: "MLA_ERR_UNSUPPORTED", -4: "MLA_ERR_WORKSPACE_TOO_SMALL", -5: "MLA_ERR_HIP"}
+          -3: "MLA_ERR_UNSUPPORTED", -4: "MLA_ERR_WORKSPACE_TOO_SMALL", -5: "MLA_ERR_HIP",
+          -6: "MLA_ERR_SCRATCH_LIMIT"}
 
 
 class PlanInfo(ctypes.Structure):
@@ -27,6 +28,7 @@ _SIGS = {
     "mla_decode_plan": [_P, _I, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PlanInfo), _P],
     "mla_decode": [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
                    ctypes.c_size_t, _P, _P, _P],
+    "mla_decode_noalloc": [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P],
     "gqa_decode": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
                    ctypes.c_size_t, _P, _P, _P],
     "attn_combine": [_P, _P, _P, _I, _I, _I, _P, _P, _P],

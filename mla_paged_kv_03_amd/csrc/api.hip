@@ -4,11 +4,23 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/mla_decode.h"
 #include "kernels.h"
 #include "schedule.h"
+
+// Scratch of mla_decode_noalloc: the plan's metadata, its slot prefix and
+// the fp32 split partials, in one static device array (one copy per GPU,
+// held until the process ends). Host code never passes `scratch` itself to
+// a kernel: its name on the host is only a handle, and the device address
+// comes from hipGetSymbolAddress (noalloc_scratch below).
+constexpr size_t NOALLOC_META_BYTES = (size_t)512 << 10;
+constexpr size_t NOALLOC_SPLIT_BYTES = (size_t)512 << 10;
+constexpr size_t NOALLOC_WS_BYTES = (size_t)136 << 20;
+constexpr size_t NOALLOC_BYTES = NOALLOC_META_BYTES + NOALLOC_SPLIT_BYTES + NOALLOC_WS_BYTES;
+static __device__ __align__(256) char scratch[NOALLOC_BYTES];
 
 namespace {
 
@@ -199,6 +211,25 @@ int run_decode(int B, int T, int H, int G, int DV, int kind, const void* q, cons
   return MLA_OK;
 }
 
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// (with that device current) and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+int noalloc_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
 // Shared checks and launch of the paged KV append (both cache shapes).
 int append_common(const void* src0, const void* src1, void* dst0, void* dst1,
                   const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
@@ -267,6 +298,41 @@ int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
   return run_decode(batch, s_q, h_q, 1, MLA_DV, mla::KIND_MLA, q, kv_cache, nullptr, nullptr, block_table, cache_seqlens, num_pages,
                     max_pages_per_seq, softmax_scale, causal, sched_metadata, num_splits,
                     workspace, workspace_bytes, out, lse, stream);
+}
+
+int mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                       const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                       int32_t num_pages, int32_t max_pages_per_seq, float softmax_scale,
+                       int32_t causal, void* out, float* lse, hipStream_t stream) {
+  Geom g;
+  int rc, cus = 0;
+  if ((rc = make_geom(batch, s_q, h_q, 1, MLA_DV, 1, &g)) != MLA_OK) return rc;
+  if (batch == 0) return MLA_OK;
+  // the plan buffers live in the scratch: check the caller's pointers now,
+  // with stand-ins for those, so that nothing is enqueued on an error
+  const int32_t* stand_in = cache_seqlens;
+  if ((rc = check_decode_args(false, q, kv_cache, nullptr, block_table, cache_seqlens, num_pages,
+                              max_pages_per_seq, softmax_scale, causal, stand_in, stand_in, out,
+                              lse)) != MLA_OK)
+    return rc;
+  if ((rc = device_cus(&cus)) != MLA_OK) return rc;
+  make_geom(batch, s_q, h_q, 1, MLA_DV, cus, &g);
+  if (g.meta_bytes > NOALLOC_META_BYTES || g.split_bytes > NOALLOC_SPLIT_BYTES ||
+      g.ws_bytes > NOALLOC_WS_BYTES)
+    return MLA_ERR_SCRATCH_LIMIT;
+  void* base = nullptr;
+  if ((rc = noalloc_scratch(&base)) != MLA_OK) return rc;
+  int32_t* meta = (int32_t*)base;
+  int32_t* splits = (int32_t*)((char*)base + NOALLOC_META_BYTES);
+  void* ws = (char*)base + NOALLOC_META_BYTES + NOALLOC_SPLIT_BYTES;
+  // the plan kernel rewrites every word the decode and merge read, so
+  // nothing in the scratch needs clearing between calls
+  if (mla::launch_plan_kernel(cache_seqlens, batch, g.W, g.TH, g.G, g.DV, meta, splits, stream) !=
+      hipSuccess)
+    return MLA_ERR_HIP;
+  return run_decode(batch, s_q, h_q, 1, MLA_DV, mla::KIND_MLA, q, kv_cache, nullptr, nullptr,
+                    block_table, cache_seqlens, num_pages, max_pages_per_seq, softmax_scale,
+                    causal, meta, splits, ws, NOALLOC_WS_BYTES, out, lse, stream);
 }
 
 int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -512,6 +578,7 @@ const char* mla_status_string(int code) {
     case MLA_ERR_UNSUPPORTED: return "head dimensions or sizes not supported by this build";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than the plan requires";
     case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_SCRATCH_LIMIT: return "the call needs more than the library's static scratch";
   }
   return "unknown status";
 }

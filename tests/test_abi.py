@@ -25,13 +25,13 @@ def test_every_declared_function_is_exported(L):
     assert {"mla_decode_plan", "mla_decode", "gqa_decode", "attn_combine", "mla_kv_append",
             "gqa_kv_append", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output",
             "gqla_decode", "mla_decode_fp8", "mla_kv_append_fp8",
-            "mla_kv_quantize_fp8", "mla_check_pages"} <= set(names)
+            "mla_kv_quantize_fp8", "mla_check_pages", "mla_decode_noalloc"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
 
 def test_status_strings(L):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert L.mla_status_string(code) != b"unknown status"
     assert L.mla_status_string(7) == b"unknown status"
 
@@ -61,6 +61,22 @@ def _mla(L, **kw):
 ])
 def test_mla_decode_rejects_bad_arguments_before_device_work(L, kw, code):
     assert _mla(L, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(kv=None), -1), (dict(bt=None), -1), (dict(sl=None), -1),
+    (dict(out=None), -1), (dict(lse=None), -1), (dict(B=-1), -2), (dict(T=0), -2),
+    (dict(P=0), -2), (dict(causal=2), -2), (dict(scale=float("nan")), -2),
+    (dict(q=ctypes.c_void_p(18)), -2), (dict(T=1 << 11, H=1 << 10), -3), (dict(B=0), 0),
+])
+def test_noalloc_rejects_bad_arguments_before_device_work(L, kw, code):
+    a = dict(q=ctypes.c_void_p(16), kv=ctypes.c_void_p(32), bt=ctypes.c_void_p(48),
+             sl=ctypes.c_void_p(64), B=2, T=1, H=8, P=5, maxp=4, scale=0.07, causal=0,
+             out=ctypes.c_void_p(112), lse=ctypes.c_void_p(128))
+    a.update(kw)
+    assert L.mla_decode_noalloc(a["q"], a["kv"], a["bt"], a["sl"], a["B"], a["T"], a["H"],
+                                a["P"], a["maxp"], a["scale"], a["causal"], a["out"], a["lse"],
+                                None) == code
 
 
 def test_gqa_rejects_bad_group_count(L):
