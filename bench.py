@@ -455,6 +455,23 @@ def bench_ceilings(args):
                     # nominal: 128 bytes per clock per CU at 2.4 GHz
                     emit(f"lds_operand_{name}", steps * 1024 / sec / 1e9, "GB/s",
                          round(128 * cus * 2.4, 1), extra)
+    if which in ("write", "all"):
+        # one 256 KiB block per workgroup (a split's fp32 partial rows), one
+        # or several workgroups per CU, blocks packed or spaced apart
+        blk = 256 << 10
+        for per_cu, pad in ((1, 0), (1, 4096), (1, 65536), (4, 0), (4, 4096)):
+            grid = cus * per_cu
+            stride = blk + pad
+            buf = torch.empty(grid * stride // 4 + 64, dtype=torch.int32, device=dev)
+            def call():
+                rc = L.mla_ceiling_block_write(P(buf), blk, stride, grid, stream)
+                if rc:
+                    raise RuntimeError(f"mla_ceiling_block_write failed with {rc}")
+            sec = timed(call, max(10, n))
+            emit("hbm_block_write", grid * blk / sec / 1e9, "GB/s", HBM_PEAK_GBS,
+                 {"block_bytes": blk, "stride_bytes": stride, "workgroups": grid,
+                  "launch_us": round(sec * 1e6, 1)})
+            del buf
     if which in ("gemm", "all"):
         m = 8192
         a = torch.randn(m, m, dtype=torch.bfloat16, device=dev)
@@ -484,7 +501,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--ceiling", choices=["mfma", "stream", "lds", "ldsop", "gemm", "all"], default=None,
+    ap.add_argument("--ceiling", choices=["mfma", "stream", "lds", "ldsop", "write", "gemm", "all"], default=None,
                     help="only measure practical ceilings: bf16 MFMA loops, a streaming HBM "
                          "read, the decode's HBM -> LDS page-copy loop alone, LDS operand reads "
                          "with and without MFMAs, torch's bf16 GEMM")

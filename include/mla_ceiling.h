@@ -59,6 +59,13 @@ int mla_ceiling_lds_fill(const void* src, size_t bytes, int32_t waves, int32_t g
 int mla_ceiling_lds_operand(int32_t mode, int32_t waves, int32_t iters, int32_t grid, float* sink,
                             hipStream_t stream);
 
+/* Write block_bytes (a multiple of 16) at dst + w * stride_bytes for each
+ * workgroup w < grid (256 threads, 16-byte stores, lanes consecutive): the
+ * HBM write rate for one block per workgroup, and how it depends on the
+ * blocks' spacing. dst must hold (grid - 1) * stride_bytes + block_bytes. */
+int mla_ceiling_block_write(void* dst, size_t block_bytes, size_t stride_bytes, int32_t grid,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

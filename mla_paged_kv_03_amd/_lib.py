@@ -50,6 +50,7 @@ _SIGS = {
     "mla_ceiling_stream_read": [_P, ctypes.c_size_t, _I, _P, _P],
     "mla_ceiling_lds_fill": [_P, ctypes.c_size_t, _I, _I, _P, _P],
     "mla_ceiling_lds_operand": [_I, _I, _I, _I, _P, _P],
+    "mla_ceiling_block_write": [_P, ctypes.c_size_t, ctypes.c_size_t, _I, _P],
     "mla_profile_events": [_P, _P],
 }
 

@@ -61,6 +61,7 @@ struct Geom {
   // blocks (nrb of them per worker) over the same workers
   bool big;
   int nrb128;
+  int fix;    // per-sequence overhead units of the plan (schedule.h)
   int W;      // workers
   int TH;
   int max_slots;
@@ -91,6 +92,7 @@ int make_geom(int B, int T, int H, int G, int DV, int cus, Geom* g) {
   g->RB = G * g->nrb;
   g->big = !g->gqa && g->M >= 128;
   g->nrb128 = (g->M + 127) / 128;
+  g->fix = g->big ? sched::FIX_LATENT128 : sched::FIX_DEFAULT;
   // one workgroup per CU for the latent cache (two 72 KiB page buffers);
   // the GQA pages are 32 KiB, so two workgroups share a CU
   const int per_cu = g->gqa ? 2 : 1;
@@ -283,7 +285,7 @@ int mla_decode_plan(const int32_t* cache_seqlens, int32_t batch, int32_t s_q, in
   make_geom(batch, s_q, h_q, h_kv, head_dim_v, cus, &g);
   fill_info(g, info);
   if (!sched_metadata && !num_splits) return MLA_OK;
-  if (mla::launch_plan_kernel(cache_seqlens, batch, g.W, g.TH, g.G, g.DV, sched_metadata,
+  if (mla::launch_plan_kernel(cache_seqlens, batch, g.W, g.TH, g.G, g.DV, g.fix, sched_metadata,
                               num_splits, stream) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
@@ -327,8 +329,8 @@ int mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block
   void* ws = (char*)base + NOALLOC_META_BYTES + NOALLOC_SPLIT_BYTES;
   // the plan kernel rewrites every word the decode and merge read, so
   // nothing in the scratch needs clearing between calls
-  if (mla::launch_plan_kernel(cache_seqlens, batch, g.W, g.TH, g.G, g.DV, meta, splits, stream) !=
-      hipSuccess)
+  if (mla::launch_plan_kernel(cache_seqlens, batch, g.W, g.TH, g.G, g.DV, g.fix, meta, splits,
+                              stream) != hipSuccess)
     return MLA_ERR_HIP;
   return run_decode(batch, s_q, h_q, 1, MLA_DV, mla::KIND_MLA, q, kv_cache, nullptr, nullptr,
                     block_table, cache_seqlens, num_pages, max_pages_per_seq, softmax_scale,
@@ -536,17 +538,18 @@ int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q
   if (!sched_metadata_host && !num_splits_host) return MLA_OK;
   if (!sched_metadata_host || !num_splits_host || (batch > 0 && !seqlens_host))
     return MLA_ERR_NULL_ARG;
-  sched::write_header(sched_metadata_host, g.W, batch, g.TH, g.G, g.DV);
+  sched::write_header(sched_metadata_host, g.W, batch, g.TH, g.G, g.DV, g.fix);
   int32_t* prefix = sched::unit_prefix(sched_metadata_host, g.W);
   prefix[0] = 0;
-  for (int b = 0; b < batch; ++b) prefix[b + 1] = prefix[b] + sched::seq_units(seqlens_host[b]);
+  for (int b = 0; b < batch; ++b)
+    prefix[b + 1] = prefix[b] + sched::seq_units(seqlens_host[b], g.fix);
   for (int w = 0; w < g.W; ++w)
-    sched::worker_record(w, g.W, prefix, seqlens_host, batch,
+    sched::worker_record(w, g.W, prefix, seqlens_host, batch, g.fix,
                          sched::records(sched_metadata_host) + (size_t)w * sched::REC);
   int32_t acc = 0;
   for (int b = 0; b < batch; ++b) {
     num_splits_host[b] = acc;
-    acc += sched::seq_slots(b, g.W, prefix, seqlens_host, batch);
+    acc += sched::seq_slots(b, g.W, prefix, seqlens_host, batch, g.fix);
   }
   num_splits_host[batch] = acc;
   return MLA_OK;

@@ -49,7 +49,7 @@ constexpr int PLAN_LDS_SEQS = 8192;
 // after the W worker records), every worker record, and the exclusive prefix
 // of partial slots (B + 1 entries).
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqlens, int B, int W,
-                                                           int rows, int G, int DV,
+                                                           int rows, int G, int DV, int fix,
                                                            int32_t* meta, int32_t* slots) {
   __shared__ int buf[PLAN_WAVES];
   __shared__ int32_t s_prefix[PLAN_LDS_SEQS + 1];
@@ -60,14 +60,14 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
 
   int carry = 0, total = 0;
   if (tid == 0) {
-    sched::write_header(meta, W, B, rows, G, DV);
+    sched::write_header(meta, W, B, rows, G, DV, fix);
     prefix[0] = 0;
     s_prefix[0] = 0;
   }
   for (int base = 0; base < B; base += PLAN_THREADS) {
     const int b = base + tid;
     const int L = b < B ? seqlens[b] : 0;
-    const int v = b < B ? sched::seq_units(L) : 0;
+    const int v = b < B ? sched::seq_units(L, fix) : 0;
     const int inc = block_scan(v, buf, &total);
     if (b < B) {
       prefix[b + 1] = carry + inc;
@@ -84,12 +84,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
   const int32_t* len = in_lds ? s_len : seqlens;
 
   for (int w = tid; w < W; w += PLAN_THREADS)
-    sched::worker_record(w, W, pre, len, B, sched::records(meta) + (size_t)w * sched::REC);
+    sched::worker_record(w, W, pre, len, B, fix, sched::records(meta) + (size_t)w * sched::REC);
 
   carry = 0;
   for (int base = 0; base < B; base += PLAN_THREADS) {
     const int b = base + tid;
-    const int v = b < B ? sched::seq_slots(b, W, pre, len, B) : 0;
+    const int v = b < B ? sched::seq_slots(b, W, pre, len, B, fix) : 0;
     const int inc = block_scan(v, buf, &total);
     if (b < B) slots[b] = carry + inc - v;
     carry += total;
@@ -98,9 +98,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
 }
 
 hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int rows, int G, int DV,
-                              int32_t* meta, int32_t* slots, hipStream_t st) {
+                              int fix, int32_t* meta, int32_t* slots, hipStream_t st) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, seqlens, B, W, rows, G, DV,
-                     meta, slots);
+                     fix, meta, slots);
   return hipGetLastError();
 }
 

@@ -10,7 +10,9 @@
 //     buffered with one barrier per block, which bounds how fast a CU can
 //     fill its LDS with pages;
 //   * lds_operand_kernel: LDS reads of MFMA operands, alone and feeding
-//     32x32x16 MFMAs, at the decode's one KiB per wave per MFMA.
+//     32x32x16 MFMAs, at the decode's one KiB per wave per MFMA;
+//   * block_write_kernel: one contiguous block written per workgroup, the
+//     way the decode writes its split partials.
 // None of these is on the decode path; they calibrate its measurements.
 #include "../../include/mla_ceiling.h"
 #include "decode_device.h"
@@ -191,6 +193,16 @@ __global__ __launch_bounds__(64 * NW) void lds_operand_kernel(int iters, float* 
   sink[blockIdx.x * blockDim.x + threadIdx.x] = total;
 }
 
+// Workgroup w writes `block` bytes at dst + w * stride, each wave 1 KiB per
+// store instruction (16 bytes per lane, lanes consecutive): the decode's
+// split partials leave this way, 256 KiB per workgroup.
+__global__ __launch_bounds__(256) void block_write_kernel(char* dst, size_t block, size_t stride) {
+  const u32x4 v = {threadIdx.x, blockIdx.x, 0x3f800000u, 0u};
+  char* base = dst + blockIdx.x * stride;
+  for (size_t off = 16 * threadIdx.x; off + 16 <= block; off += 16 * 256)
+    *(u32x4*)(base + off) = v;
+}
+
 }  // namespace mla
 
 extern "C" {
@@ -264,6 +276,16 @@ int mla_ceiling_lds_operand(int32_t mode, int32_t waves, int32_t iters, int32_t 
   LDS_CASE(5, 8)
 #undef LDS_CASE
   return MLA_CEIL_ERR_ARG;
+}
+
+int mla_ceiling_block_write(void* dst, size_t block_bytes, size_t stride_bytes, int32_t grid,
+                            hipStream_t stream) {
+  if (!dst || grid < 1 || block_bytes < 16 || (block_bytes & 15) || stride_bytes < block_bytes ||
+      (stride_bytes & 15) || ((uintptr_t)dst & 15))
+    return MLA_CEIL_ERR_ARG;
+  hipLaunchKernelGGL(mla::block_write_kernel, dim3(grid), dim3(256), 0, stream, (char*)dst,
+                     block_bytes, stride_bytes);
+  return hipGetLastError() == hipSuccess ? 0 : MLA_CEIL_ERR_HIP;
 }
 
 }  // extern "C"

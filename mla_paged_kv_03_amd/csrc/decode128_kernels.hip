@@ -231,17 +231,22 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
     // flight, so that the two latencies overlap
     bf16x8 qf[R128_KC];
     auto load_q = [&]() {
-      // with a negative softmax scale the queries are negated (exactly: a
-      // sign flip) and the scale's magnitude used, so scale * score keeps
-      // its value and the row max is always a max of raw scores
-      const uint32_t flip = scale_neg ? 0x80008000u : 0u;
       const uint16_t* qrow = a.q + ((size_t)b * TH + rho) * LY::D;
 #pragma unroll
       for (int c = 0; c < R128_KC; ++c) {
-        u32x4 x = row_ok ? *(const u32x4*)(qrow + 16 * c + 8 * hf) : u32x4{0u, 0u, 0u, 0u};
-        x ^= flip;
+        const u32x4 x = row_ok ? *(const u32x4*)(qrow + 16 * c + 8 * hf) : u32x4{0u, 0u, 0u, 0u};
         qf[c] = __builtin_bit_cast(bf16x8, x);
       }
+    };
+    // With a negative softmax scale the queries are negated (exactly: a sign
+    // flip) and the scale's magnitude used, so scale * score keeps its value
+    // and the row max is always a max of raw scores. The flip waits until
+    // the first page has landed, so that the query loads overlap its copies.
+    auto flip_q = [&]() {
+      const uint32_t flip = scale_neg ? 0x80008000u : 0u;
+#pragma unroll
+      for (int c = 0; c < R128_KC; ++c)
+        qf[c] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[c]) ^ flip);
     };
     const int vis = a.causal ? min(L - a.T + 1 + t, L) : L;
     // keys below this are visible to every row of the workgroup
@@ -307,6 +312,9 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
         wait_vm<0>();
         barrier();
         lds_char* const buf = lds_p + cur * LY::TILE;
+        if constexpr (MODE == PASS_FIRST_REF) {
+          if (j == p0) flip_q();
+        }
 
         // ---- S^T = K Q^T for the page's two 32-key blocks ----
         auto k_frag = [&](int st) -> bf16x8 {

@@ -129,6 +129,6 @@ hipError_t launch_check_pages(const int32_t* block_table, const int32_t* seqlens
 // Schedule: signature, worker records and unit prefix into meta, slot
 // prefix into slots.
 hipError_t launch_plan_kernel(const int32_t* seqlens, int B, int W, int rows, int G, int DV,
-                              int32_t* meta, int32_t* slots, hipStream_t st);
+                              int fix, int32_t* meta, int32_t* slots, hipStream_t st);
 
 }  // namespace mla

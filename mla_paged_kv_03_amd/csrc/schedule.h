@@ -4,11 +4,14 @@
 // FlashAttention (KO), section "FlashAttention-2 (2023)", credits better
 // parallelism and work partitioning across the GPU; the FlashMLA blog
 // ("기술 기반") asks for efficient variable-length handling. Here the work
-// of sequence b is FIXED_UNITS overhead units (loading its queries, writing
-// its result) followed by one unit per 64-token page; the units of the whole
+// of sequence b is `fix` overhead units (loading its queries, writing its
+// result) followed by one unit per 64-token page; the units of the whole
 // batch are concatenated and cut into num_workers equal contiguous ranges of
 // `chunk` units. A sequence whose pages fall into several ranges is split;
 // each piece writes a partial result that a log-sum-exp merge finishes.
+// `fix` is part of the plan (FIX_LATENT128 for the 128-row latent decode,
+// whose per-sequence queries and output weigh several pages, FIX_DEFAULT
+// otherwise) and is recorded in the plan's signature.
 //
 // Every function here is plain arithmetic usable on the host (for the
 // host-side checker) and on the device (for the plan kernel).
@@ -25,7 +28,8 @@
 namespace sched {
 
 constexpr int PAGE = 64;
-constexpr int FIXED_UNITS = 2;
+constexpr int FIX_DEFAULT = 2;
+constexpr int FIX_LATENT128 = 6;
 constexpr int REC = 8;  // int32 per worker record
 
 // The metadata opens with a signature of the geometry the plan was made for
@@ -36,16 +40,16 @@ constexpr int REC = 8;  // int32 per worker record
 // value width is passed in.
 constexpr int HDR = 8;
 constexpr int32_t PLAN_MAGIC = 0x4D4C4150;  // "PALM" in memory order
-enum : int { H_MAGIC = 0, H_W = 1, H_B = 2, H_ROWS = 3, H_G = 4, H_DV = 5 };
+enum : int { H_MAGIC = 0, H_W = 1, H_B = 2, H_ROWS = 3, H_G = 4, H_DV = 5, H_FIX = 6 };
 
-SCHED_HD void write_header(int32_t* hdr, int W, int B, int rows, int G, int DV) {
+SCHED_HD void write_header(int32_t* hdr, int W, int B, int rows, int G, int DV, int fix) {
   hdr[H_MAGIC] = PLAN_MAGIC;
   hdr[H_W] = W;
   hdr[H_B] = B;
   hdr[H_ROWS] = rows;
   hdr[H_G] = G;
   hdr[H_DV] = DV;
-  hdr[6] = 0;
+  hdr[H_FIX] = fix;
   hdr[7] = 0;
 }
 
@@ -67,7 +71,7 @@ enum : int {
 };
 
 SCHED_HD int seq_pages(int32_t L) { return L > 0 ? (L + PAGE - 1) / PAGE : 0; }
-SCHED_HD int seq_units(int32_t L) { return seq_pages(L) + FIXED_UNITS; }
+SCHED_HD int seq_units(int32_t L, int fix) { return seq_pages(L) + fix; }
 
 // Largest b in [0, B) with prefix[b] <= u (prefix strictly increasing,
 // prefix[0] = 0 <= u).
@@ -87,7 +91,7 @@ SCHED_HD int chunk_units(int32_t total_units, int W) {
 
 // Record of worker w. prefix has B + 1 entries (prefix[B] = total units).
 SCHED_HD void worker_record(int w, int W, const int32_t* prefix, const int32_t* seqlens,
-                            int B, int32_t* rec) {
+                            int B, int fix, int32_t* rec) {
   const int32_t C = prefix[B];
   const int chunk = chunk_units(C, W);
   const int64_t lo = (int64_t)w * chunk;
@@ -99,13 +103,13 @@ SCHED_HD void worker_record(int w, int W, const int32_t* prefix, const int32_t* 
   const int64_t hi = (lo + chunk < C) ? lo + chunk : C;
   const int bs = find_seq(prefix, B, lo);
   const int be = find_seq(prefix, B, hi - 1);
-  int64_t ps = lo - prefix[bs] - FIXED_UNITS;
+  int64_t ps = lo - prefix[bs] - fix;
   if (ps < 0) ps = 0;
   const int ne = seq_pages(seqlens[be]);
-  int64_t pe = hi - prefix[be] - FIXED_UNITS;
+  int64_t pe = hi - prefix[be] - fix;
   if (pe < 0) pe = 0;
   if (pe > ne) pe = ne;
-  const int first_w = (prefix[bs] + FIXED_UNITS) / chunk;
+  const int first_w = (prefix[bs] + fix) / chunk;
   rec[R_B_START] = bs;
   rec[R_P_START] = (int32_t)ps;
   rec[R_B_END] = be;
@@ -131,17 +135,19 @@ SCHED_HD void page_range(const int32_t* rec, int b, int bs, int be, int npg, int
 }
 
 // Number of workers that process pages of sequence b (1 for an empty one).
-SCHED_HD int seq_split_count(int b, int W, const int32_t* prefix, const int32_t* seqlens, int B) {
+SCHED_HD int seq_split_count(int b, int W, const int32_t* prefix, const int32_t* seqlens, int B,
+                             int fix) {
   if (seq_pages(seqlens[b]) == 0) return 1;
   const int chunk = chunk_units(prefix[B], W);
-  const int first = (prefix[b] + FIXED_UNITS) / chunk;
+  const int first = (prefix[b] + fix) / chunk;
   const int last = (prefix[b + 1] - 1) / chunk;
   return last - first + 1;
 }
 
 // Partial-result slots of sequence b: none when one worker finishes it.
-SCHED_HD int seq_slots(int b, int W, const int32_t* prefix, const int32_t* seqlens, int B) {
-  const int n = seq_split_count(b, W, prefix, seqlens, B);
+SCHED_HD int seq_slots(int b, int W, const int32_t* prefix, const int32_t* seqlens, int B,
+                       int fix) {
+  const int n = seq_split_count(b, W, prefix, seqlens, B, fix);
   return n > 1 ? n : 0;
 }
 

@@ -12,7 +12,7 @@ from mla_paged_kv_03_amd import _lib, mla_decode_plan_host, PlanInfo
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 REC = 8
 HDR = 8  # plan signature words ahead of the worker records
-FIXED = 2
+FIX_DEFAULT, FIX_LATENT128 = 2, 6  # schedule.h
 
 
 @pytest.fixture(scope="module")
@@ -242,9 +242,13 @@ def test_schedule_covers_every_page_once(seqlens, shape, cus):
     assert sorted(slot_users) == list(range(splits[-1]))
     for b in range(len(seqlens)):
         assert splits[b + 1] - splits[b] != 1, "a single piece never uses a slot"
-    # the prefix of work units follows the per-sequence cost
+    # the prefix of work units follows the per-sequence cost: its pages and
+    # the plan's overhead units, recorded in the signature (more for the
+    # 128-row latent decode, whose queries and output weigh several pages)
+    fix = int(meta[6])
+    assert fix == (FIX_LATENT128 if (G == 1 and dv == 512 and T * H >= 128) else FIX_DEFAULT)
     units = meta[HDR + W * REC:HDR + W * REC + len(seqlens) + 1]
-    expect = np.concatenate([[0], np.cumsum([(int(L) + 63) // 64 + FIXED for L in seqlens])])
+    expect = np.concatenate([[0], np.cumsum([(int(L) + 63) // 64 + fix for L in seqlens])])
     assert np.array_equal(units, expect)
 
 
@@ -253,7 +257,7 @@ def test_schedule_balances_work():
     meta, splits, info = mla_decode_plan_host(seqlens, 2, 128, num_cus=256)
     W = info.num_workers
     loads = [meta[HDR + w * REC + 7] - meta[HDR + w * REC + 6] for w in range(W)]
-    total = sum((int(L) + 63) // 64 + FIXED for L in seqlens)
+    total = sum((int(L) + 63) // 64 + int(meta[6]) for L in seqlens)
     chunk = -(-total // W)
     assert max(loads) <= chunk and sum(loads) == total
 
@@ -269,14 +273,16 @@ def test_workspace_size_matches_slot_bound():
                                    (3, 7, 1, 512)])
 def test_plan_opens_with_its_geometry(shape):
     """The metadata starts with a signature: a fixed tag, the worker count,
-    the batch, the rows per sequence (s_q * h_q), the KV heads and the value
-    width; the decode and merge kernels compare it with their own call."""
+    the batch, the rows per sequence (s_q * h_q), the KV heads, the value
+    width and the plan's per-sequence overhead units; the decode and merge
+    kernels compare the first six with their own call."""
     T, H, G, dv = shape
     seqlens = [100, 0, 5000]
     meta, splits, info = mla_decode_plan_host(seqlens, T, H, G, dv, num_cus=256)
     assert info.metadata_bytes == 4 * (HDR + info.num_workers * REC + len(seqlens) + 1)
     assert list(meta[:6]) == [0x4D4C4150, info.num_workers, len(seqlens), T * H, G, dv]
-    assert list(meta[6:8]) == [0, 0]
+    fix = FIX_LATENT128 if (G == 1 and dv == 512 and T * H >= 128) else FIX_DEFAULT
+    assert list(meta[6:8]) == [fix, 0]
 
 
 def test_page_range_is_clamped_to_current_lengths(tmp_path):
@@ -304,11 +310,11 @@ int main(int argc, char** argv) {
   for (int b = 0; b < B; ++b) { Lp[b] = atoi(argv[2 + b]); Lc[b] = atoi(argv[2 + B + b]); }
   int32_t* prefix = sched::unit_prefix(meta.data(), W);
   prefix[0] = 0;
-  for (int b = 0; b < B; ++b) prefix[b + 1] = prefix[b] + sched::seq_units(Lp[b]);
+  for (int b = 0; b < B; ++b) prefix[b + 1] = prefix[b] + sched::seq_units(Lp[b], FIX);
   long pairs = 0;
   for (int w = 0; w < W; ++w) {
     int32_t* rec = sched::records(meta.data()) + w * sched::REC;
-    sched::worker_record(w, W, prefix, Lp.data(), B, rec);
+    sched::worker_record(w, W, prefix, Lp.data(), B, FIX, rec);
     for (int b = rec[sched::R_B_START]; b <= rec[sched::R_B_END]; ++b) {
       const int npg = sched::seq_pages(Lc[b]);
       int p0, p1;
@@ -323,10 +329,12 @@ int main(int argc, char** argv) {
   return 0;
 }
 """)
-    exe = tmp_path / "range"
-    subprocess.run([gxx, "-O1", "-std=c++17", "-I", csrc, str(src), "-o", str(exe)], check=True)
     rng = np.random.default_rng(9)
-    for W in (1, 7, 64, 128):
+    for fix, W in [(f, w) for f in (FIX_DEFAULT, FIX_LATENT128) for w in (1, 7, 64, 128)]:
+        exe = tmp_path / f"range{fix}"
+        if not exe.exists():
+            subprocess.run([gxx, "-O1", "-std=c++17", f"-DFIX={fix}", "-I", csrc, str(src), "-o",
+                            str(exe)], check=True)
         for _ in range(4):
             B = int(rng.integers(1, 40))
             plan_L = rng.integers(0, 5000, size=B)
