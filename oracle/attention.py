@@ -129,6 +129,50 @@ def attend_two_pass(q, k_cache, block_table, seqlens, scale, causal,
     return out, lse
 
 
+def value_spread(q, k_cache, block_table, seqlens, scale, causal, v_cache=None, d_v=None):
+    """Per output element, how far the values it averages lie from the
+    output: the attention-weighted standard deviation of V,
+    sqrt(sum_j w_j v_j^2 - (sum_j w_j v_j)^2), and the weighted mean of |V|,
+    sum_j w_j |v_j|, with w the softmax weights of that row (the same weights
+    as attend_two_pass); plus the number of keys the row sees. They size the
+    error of a decode whose products round their weights: an output
+    sum_j w_j v_j moves by sum_j dw_j (v_j - out) when the weights move by dw
+    with sum_j dw_j = 0. Returns sd [B, T, H, Dv], mean_abs [B, T, H, Dv] and
+    nkeys [B, T, H] (0 where the row sees nothing)."""
+    B, T, H, D = q.shape
+    G = k_cache.shape[2]
+    hpg = _heads_per_group(H, G)
+    if d_v is None:
+        d_v = D if v_cache is None else v_cache.shape[3]
+    sigma = scale_as_received(scale)
+    sd = np.zeros((B, T, H, d_v))
+    mean_abs = np.zeros((B, T, H, d_v))
+    nkeys = np.zeros((B, T, H), dtype=np.int64)
+    for b in range(B):
+        L = int(seqlens[b])
+        if L <= 0:
+            continue
+        K, V = _sequence_kv(k_cache, v_cache, d_v, block_table[b], L)
+        qb = bf16_to_f64(q[b])
+        for g in range(G):
+            hs = slice(g * hpg, (g + 1) * hpg)
+            s = sigma * np.matmul(qb[:, hs, :], K[:, g, :].T)   # [T, hpg, L]
+            Vg = V[:, g, :]
+            for t in range(T):
+                hi = visible_keys(L, T, t, causal)
+                if hi <= 0:
+                    continue
+                st = s[t, :, :hi]
+                e = np.exp(st - st.max(axis=1, keepdims=True))
+                w = e / e.sum(axis=1, keepdims=True)            # [hpg, hi]
+                mean = w @ Vg[:hi]
+                second = w @ (Vg[:hi] ** 2)
+                sd[b, t, hs] = np.sqrt(np.maximum(second - mean ** 2, 0.0))
+                mean_abs[b, t, hs] = w @ np.abs(Vg[:hi])
+                nkeys[b, t, hs] = hi
+    return sd, mean_abs, nkeys
+
+
 def softmax_weights(q, k_cache, block_table, seqlens, scale, causal, b, t):
     """The attention weights of every head of query (b, t) over the keys it
     sees: [H, visible]. Used to check that each row sums to one."""

@@ -46,19 +46,28 @@ def run_gpu(d, t, plan=None, out=None, lse=None):
     return o.float().cpu().double().numpy(), l.cpu().double().numpy()
 
 
-def run_oracle(d, batch_idx=None):
+def run_oracle(d, batch_idx=None, spread=False):
+    """Oracle out and lse of the chosen sequences; with spread=True also the
+    value spread (oracle.value_spread) that sizes the tighter allowance."""
     cfg = d["cfg"]
     idx = np.arange(cfg.batch) if batch_idx is None else np.asarray(batch_idx)
     q = d["q"][idx]
     bt = d["block_table"][idx]
     L = d["cache_seqlens"][idx]
     if cfg.kind == "mla":
-        return oracle.attend_two_pass(q, d["kv"], bt, L, cfg.scale, cfg.causal, d_v=cfg.d_v)
-    return oracle.attend_two_pass(q, d["k"], bt, L, cfg.scale, cfg.causal, v_cache=d["v"])
+        args = (q, d["kv"], bt, L, cfg.scale, cfg.causal)
+        kw = {"d_v": cfg.d_v}
+    else:
+        args = (q, d["k"], bt, L, cfg.scale, cfg.causal)
+        kw = {"v_cache": d["v"]}
+    out, lse = oracle.attend_two_pass(*args, **kw)
+    if not spread:
+        return out, lse
+    return out, lse, oracle.value_spread(*args, **kw)
 
 
-def check(out, lse, ref_out, ref_lse, what):
-    res = oracle.compare(out, lse, ref_out, ref_lse)
+def check(out, lse, ref_out, ref_lse, what, spread=None):
+    res = oracle.compare(out, lse, ref_out, ref_lse, spread=spread)
     log(f"[parity] {what}: " + ", ".join(f"{k}={v}" for k, v in res.items()))
     assert res["ok"], f"{what}: {res}"
     return res

@@ -463,3 +463,103 @@ def test_tolerance_checker():
     got = ref.copy()
     got[0, :100] = 1.0078125                   # every element one step off: rel-L2 fails
     assert not compare(got, np.array([0.5, -np.inf]), ref, lse_ref)["ok"]
+
+
+def test_tolerance_with_the_arithmetic_bound():
+    """With the value spread given, an element passes within half a bf16 step
+    of the exact value plus the bound of the decode's arithmetic, which is
+    tighter than one whole step where the values are concentrated."""
+    from oracle import compare, rounding_allowance
+    ref = np.zeros((1, 101))
+    ref[0, :100], ref[0, 100] = 1.0, 5.0
+    lse_ref = np.array([0.5])
+    sd = np.zeros_like(ref)                     # every weight on one value
+    mean_abs = np.abs(ref)
+    nkeys = np.array([1])
+    spread = (sd, mean_abs, nkeys)
+    half = 2.0 ** -6                            # half a bf16 step at 5
+    allow = rounding_allowance(ref, spread)
+    assert allow[0, 100] == half + 17 * 2.0 ** -24 * 5.0
+    got = ref.copy()
+    got[0, 100] = 5.0 + 0.9 * half              # within half a step: passes
+    assert compare(got, lse_ref, ref, lse_ref, spread=spread)["ok"]
+    got[0, 100] = 5.03125                       # a whole step: only the loose rule passes it
+    assert not compare(got, lse_ref, ref, lse_ref, spread=spread)["ok"]
+    assert compare(got, lse_ref, ref, lse_ref)["ok"]
+    # a wide spread of values widens the bound by 2^-7 of its deviation
+    wide = (np.full_like(ref, 2.0), mean_abs, nkeys)
+    assert rounding_allowance(ref, wide)[0, 100] == half + 2.0 ** -6 + 17 * 2.0 ** -24 * 5.0
+
+
+# ------------------------------------------------------------ value spread
+def test_value_spread_single_key_and_identical_keys():
+    """One visible key: the weight is 1, so the deviation is 0 and the mean
+    |v| is |v| of that key. Identical keys: equal weights, so the deviation
+    is the population standard deviation of V over the keys and the mean
+    |v| their plain mean (numpy's std and mean, not the oracle)."""
+    from oracle import gather_pages, value_spread
+    d = tiny("mla")
+    cfg = d["cfg"]
+    sd, ma, nk = run(value_spread, d)
+    b = 1                                        # length 1
+    v = bf16_to_f64(d["kv"][d["block_table"][b, 0], 0, 0, :cfg.d_v])
+    assert np.all(sd[b] == 0.0) and np.allclose(ma[b], np.abs(v)[None, None, :], rtol=0, atol=0)
+    assert np.all(nk[b] == 1) and np.all(nk[0] == 0)
+    # identical scores: the columns past d_v (the part of the key row that is
+    # not V) are made equal on every row of sequence 2, and the query is
+    # zero on the first d_v columns, so every key scores the same while V
+    # still differs from row to row
+    kv = d["kv"].copy()
+    L = int(d["cache_seqlens"][2])
+    pages = d["block_table"][2, :(L + 63) // 64]
+    for p in pages:
+        kv[p, :, 0, cfg.d_v:] = kv[pages[0], 0, 0, cfg.d_v:]
+    q = d["q"].copy()
+    q[2, :, :, :cfg.d_v] = 0
+    sd2, ma2, _ = value_spread(q, kv, d["block_table"], d["cache_seqlens"], cfg.scale,
+                               cfg.causal, d_v=cfg.d_v)
+    V = gather_pages(kv, d["block_table"][2], L)[:, 0, :cfg.d_v]
+    np.testing.assert_allclose(sd2[2, 0, 0], V.std(axis=0), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(ma2[2, 0, 0], np.abs(V).mean(axis=0), rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("name", ["mla_causal2", "gqa_causal"])
+def test_value_spread_brute_force(name):
+    """Against explicit loops over rows, keys and columns on tiny inputs,
+    with the softmax written out per row."""
+    from oracle import value_spread
+    d = tiny(name)
+    cfg = d["cfg"]
+    sd, ma, nk = run(value_spread, d)
+    B, T, H, _ = d["q"].shape
+    G = cfg.h_kv
+    for b in range(B):
+        L = int(d["cache_seqlens"][b])
+        for t in range(T):
+            vis = min(max(L - T + 1 + t, 0), L) if cfg.causal else L
+            for h in range(H):
+                g = h // (H // G)
+                qv = bf16_to_f64(d["q"][b, t, h])
+                s, vals = [], []
+                for j in range(vis):
+                    page = int(d["block_table"][b, j // 64])
+                    if cfg.kind == "mla":
+                        row = bf16_to_f64(d["kv"][page, j % 64, g])
+                        k, v = row, row[:cfg.d_v]
+                    else:
+                        k = bf16_to_f64(d["k"][page, j % 64, g])
+                        v = bf16_to_f64(d["v"][page, j % 64, g])
+                    s.append(float(np.float32(cfg.scale)) * float(k @ qv))
+                    vals.append(v)
+                assert nk[b, t, h] == vis
+                if vis == 0:
+                    continue
+                s = np.array(s)
+                w = np.exp(s - s.max())
+                w /= w.sum()
+                vals = np.array(vals)
+                mean = (w[:, None] * vals).sum(axis=0)
+                var = (w[:, None] * (vals - mean) ** 2).sum(axis=0)
+                np.testing.assert_allclose(sd[b, t, h], np.sqrt(var), rtol=1e-7, atol=1e-9)
+                np.testing.assert_allclose(ma[b, t, h], (w[:, None] * np.abs(vals)).sum(axis=0),
+                                           rtol=1e-12, atol=1e-15)

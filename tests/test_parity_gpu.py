@@ -63,25 +63,15 @@ def test_small_shapes_match_oracle(dev, name):
     d = inputs(cfg, seed=11)
     log(f"[case] {name} seqlens={list(d['cache_seqlens'])}")
     out, lse = run_gpu(d, to_device(d, dev))
-    ref_out, ref_lse = run_oracle(d)
-    check(out, lse, ref_out, ref_lse, name)
+    ref_out, ref_lse, spread = run_oracle(d, spread=True)
+    check(out, lse, ref_out, ref_lse, name, spread=spread)
 
 
 # ------------------------------------------------------- the five configs
-def _sample(cfg, d, k=6):
-    """Sequences to check against the oracle at full size: the shortest,
-    the longest, and a seeded random pick."""
-    L = d["cache_seqlens"]
-    rng = np.random.default_rng(1234)
-    pick = {int(np.argmin(L)), int(np.argmax(L))}
-    pick |= set(int(x) for x in rng.choice(cfg.batch, size=min(k, cfg.batch), replace=False))
-    ones = np.nonzero(L == 1)[0]
-    pick |= set(int(x) for x in ones[:2])
-    return sorted(pick)
-
-
 @pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_config_matches_oracle(dev, idx):
+    """Every sequence of each configuration at full size, in the launch
+    configuration bench.py times, against the oracle."""
     import torch
     cfg = CONFIGS[idx]
     log(f"[case] config {idx} {cfg.name}: generating inputs")
@@ -94,10 +84,9 @@ def test_config_matches_oracle(dev, idx):
     # at any size: rows with keys have finite lse; rows without are exactly empty
     if not cfg.causal:
         assert np.array_equal(empty_rows.any(axis=(1, 2)), L == 0)
-    b_idx = list(range(cfg.batch)) if idx == 1 else _sample(cfg, d)
-    log(f"[case] config {idx}: oracle on sequences {b_idx}")
-    ref_out, ref_lse = run_oracle(d, b_idx)
-    check(out[b_idx], lse[b_idx], ref_out, ref_lse, f"config {idx} ({cfg.name})")
+    log(f"[case] config {idx}: oracle on all {cfg.batch} sequences")
+    ref_out, ref_lse, spread = run_oracle(d, spread=True)
+    check(out, lse, ref_out, ref_lse, f"config {idx} ({cfg.name})", spread=spread)
     del t
     torch.cuda.empty_cache()
 
@@ -338,5 +327,5 @@ def test_scores_climbing_from_page_to_page(dev, kind, period):
     pages = int(((d["cache_seqlens"] + 63) // 64).sum())
     assert pages > 2 * plan.info.num_workers  # several pages per worker
     out, lse = run_gpu(d, t, plan=plan)
-    ref_out, ref_lse = run_oracle(d)
-    check(out, lse, ref_out, ref_lse, f"climbing scores ({kind}, period {period})")
+    ref_out, ref_lse, spread = run_oracle(d, spread=True)
+    check(out, lse, ref_out, ref_lse, f"climbing scores ({kind}, period {period})", spread=spread)
