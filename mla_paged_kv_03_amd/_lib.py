@@ -6,7 +6,9 @@ import os
 import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmla_decode.so")
+# MLA_DECODE_LIB selects another build of the same library (the tests use it
+# for the host-sanitizer build); the default is the in-tree build.
+LIB_PATH = os.environ.get("MLA_DECODE_LIB") or os.path.join(PKG, "libmla_decode.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "mla_decode.h")
 
 MLA_OK = 0
