@@ -521,21 +521,30 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
       constexpr int PITCH = 528;  // staged row: 128 fp32 + 16 bytes of bank skew
       static_assert(R128_WAVES * 32 * PITCH <= 2 * LY::TILE, "staging fits the page buffers");
       lds_char* const stage = lds_p + wave * (32 * PITCH);
-      const int rr = lane >> 5, cc = lane & 31;  // read-back: row 2i + rr, 16 bytes cc
-      // the wave's first row, and this lane's element offset from it
-      const int row0 = rb * 128 + wave * 32;
-      const uint32_t lane_el = (uint32_t)(rr * LY::DV + 4 * cc);
-      // the row bases live in VGPRs: the sequence loop keeps every scalar
-      // register busy
-      uint64_t part_addr = (uint64_t)(a.part_o + (slot * TH + row0) * LY::DV);
-      uint64_t out_addr = (uint64_t)(a.out + ((size_t)b * TH + row0) * LY::DV);
-      asm volatile("" : "+v"(part_addr), "+v"(out_addr));
-      float* const part_base = (float*)part_addr;
-      uint16_t* const out_base = (uint16_t*)out_addr;
+      const int row0 = rb * 128 + wave * 32;  // the wave's first row
+      // the row bases stay global pointers: generic ones would make the
+      // stores FLAT, which also count against the LDS counter, so every
+      // staging read would wait for the stores before it
+      __attribute__((address_space(1))) float* const part_base =
+          (__attribute__((address_space(1))) float*)(a.part_o + (slot * TH + row0) * LY::DV);
+      __attribute__((address_space(1))) uint16_t* const out_base =
+          (__attribute__((address_space(1))) uint16_t*)(a.out + ((size_t)b * TH + row0) * LY::DV);
       auto staged = [&](auto part_tag) {
         constexpr bool PART = decltype(part_tag)::value;
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
+          // Lane offsets are formed again from the lane index in every
+          // chunk: kept from before the page loop they would be spilled
+          // registers, and a reload waits for every store issued before it
+          // (the memory counter retires in order).
+          int lid = (int)threadIdx.x;
+          asm volatile("" : "+v"(lid));
+          const int ln = lid & 31, lh = (lid >> 5) & 1;
+          // staging: lane (n, hf) writes row n; read-back: lane (cc, rr)
+          // reads 16 bytes cc of row 2i + rr
+          const uint32_t wr = (uint32_t)(ln * PITCH + 16 * lh);
+          const uint32_t rd = (uint32_t)(lh * PITCH + 16 * ln);
+          const uint32_t el = (uint32_t)(lh * LY::DV + 4 * ln + 128 * ch);
 #pragma unroll
           for (int t4 = 0; t4 < 4; ++t4) {
             const int tt = 4 * ch + t4;
@@ -543,23 +552,20 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
             for (int q = 0; q < 4; ++q) {
               const f32x4 z = {o[tt][4 * q] * sc_o, o[tt][4 * q + 1] * sc_o,
                                o[tt][4 * q + 2] * sc_o, o[tt][4 * q + 3] * sc_o};
-              *(__attribute__((address_space(3))) f32x4*)(stage + n * PITCH +
-                                                           4 * (32 * t4 + 8 * q + 4 * hf)) = z;
+              *(__attribute__((address_space(3))) f32x4*)(stage + wr + 4 * (32 * t4 + 8 * q)) = z;
             }
             __builtin_amdgcn_sched_barrier(0);
           }
           // a wave's LDS accesses run in issue order: the reads see the writes
-          uint32_t el = lane_el + 128 * ch;
-          asm volatile("" : "+v"(el));  // one running offset, not 16 precomputed ones
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const f32x4 v = *(const __attribute__((address_space(3))) f32x4*)(
-                stage + (2 * i + rr) * PITCH + 16 * cc);
+            const f32x4 v =
+                *(const __attribute__((address_space(3))) f32x4*)(stage + rd + 2 * i * PITCH);
             if constexpr (PART) {
-              *(f32x4*)(part_base + el + 2 * i * LY::DV) = v;
+              *(__attribute__((address_space(1))) f32x4*)(part_base + el + 2 * i * LY::DV) = v;
             } else {
               const u32x2 z = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-              *(u32x2*)(out_base + el + 2 * i * LY::DV) = z;
+              *(__attribute__((address_space(1))) u32x2*)(out_base + el + 2 * i * LY::DV) = z;
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -579,9 +585,10 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
                              o[tt][4 * q + 2] * sc_o, o[tt][4 * q + 3] * sc_o};
             const uint32_t el = (uint32_t)(n * LY::DV + 32 * tt + 8 * q + 4 * hf);
             if constexpr (PART) {
-              *(f32x4*)(part_base + el) = z;
+              *(__attribute__((address_space(1))) f32x4*)(part_base + el) = z;
             } else {
-              *(u32x2*)(out_base + el) = u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
+              *(__attribute__((address_space(1))) u32x2*)(out_base + el) =
+                  u32x2{pack_bf16x2(z[0], z[1]), pack_bf16x2(z[2], z[3])};
             }
           }
           __builtin_amdgcn_sched_barrier(0);
