@@ -38,7 +38,17 @@ METRIC = "MLA decode TFLOPS + HBM GB/s (% MI355X peak); decode tokens/s at B=64"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # dense bf16: 256 CU x 2.4 GHz x 4096 flop/clk
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "mla_paged_kv_03_amd", "csrc", "decode_kernels.hip")
+CSRC = os.path.join(ROOT, "mla_paged_kv_03_amd", "csrc")
+
+
+def decode_kernel_of(cfg, fp8=False):
+    """(kernel name, source file) of the decode kernel a configuration runs:
+    the 128-row latent kernel for a bf16 latent cache with s_q * h_q >= 128,
+    else the 64-row kernel (GQA, FP8 cache, fewer rows)."""
+    if cfg.kind == "mla" and not fp8 and cfg.s_q * cfg.h_q >= 128:
+        return "decode128_kernel", os.path.join(CSRC, "decode128_kernels.hip")
+    kind = "gqa" if cfg.kind == "gqa" else "mla fp8" if fp8 else "mla"
+    return f"decode_kernel ({kind})", os.path.join(CSRC, "decode_kernels.hip")
 
 
 def algorithmic_work(d, fp8=False):
@@ -63,10 +73,11 @@ def algorithmic_work(d, fp8=False):
     return {"bytes": kv + qb + ob, "kv_bytes": kv, "flops": flops, "rows": rows}
 
 
-def stored_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, "hbm_traffic_mla_decode_dsv3_b64.md")
+def stored_traffic(workload, kernel_src):
+    """HBM bytes per decode launch of `workload` from its committed
+    rocprofv3 counter summary, if that was taken on the current source of
+    the kernel it runs; else None."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -74,7 +85,7 @@ def stored_traffic():
     m2 = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     if not (m1 and m2):
         return None
-    cur = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    cur = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
     return int(m1.group(1)) if m2.group(1) == cur else None
 
 
@@ -651,7 +662,8 @@ def main():
     gbs = work["bytes"] / s / 1e9
     k_gbs = work["bytes"] / (kern_avg * 1e-3) / 1e9
     k_tflops = work["flops"] / (kern_avg * 1e-3) / 1e12
-    traffic = None if fp8 else stored_traffic()
+    kname, ksrc = decode_kernel_of(cfg, fp8)
+    traffic = None if fp8 else stored_traffic(cfg.name, ksrc)
     bound = "hbm" if work["flops"] / work["bytes"] < MFMA_BF16_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3 \
         else "mfma"
     if bound == "hbm":
@@ -661,8 +673,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic}
-    roof["kernel"] = f"decode_kernel ({'gqa' if cfg.kind == 'gqa' else 'mla fp8' if fp8 else 'mla'})"
+    roof["kernel"] = kname
     roof["kernel_avg_us"] = round(kern_avg * 1e3, 2)
+    roof["kernel_median_us"] = round(float(np.median(kern_ms)) * 1e3, 2)
     roof["algorithmic_bytes_per_launch"] = work["bytes"]
     roof["algorithmic_flops_per_launch"] = work["flops"]
 
