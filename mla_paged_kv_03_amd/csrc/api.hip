@@ -506,11 +506,13 @@ int gqla_expand_kv(const void* kv_rows, const void* w_uk, const void* w_uv, void
   a.a = (const uint16_t*)kv_rows;
   a.M = n_rows;
   a.G = h_kv;
-  // workgroups: about one per CU, in slices of 8 (one per XCD) per group
+  // workgroups: about one per CU, in slices of 8 (one per XCD) per pair of
+  // groups (a workgroup expands two groups)
   int cus = 0;
   if (device_cus(&cus) != MLA_OK) return MLA_ERR_HIP;
-  const int per_group = (cus + h_kv - 1) / h_kv;
-  a.n_slices = 8 * ((per_group + 7) / 8);
+  const int pairs = (h_kv + 1) / 2;
+  const int per_pair = (cus + pairs - 1) / pairs;
+  a.n_slices = 8 * ((per_pair + 7) / 8);
   // K: group g's columns 0..127 of each expanded row, plus the shared rope
   a.w = (const uint16_t*)w_uk;
   a.c = (uint16_t*)k_rows;
