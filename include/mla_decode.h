@@ -254,7 +254,8 @@ int gqa_kv_append(const void* new_k, const void* new_v, void* k_cache, void* v_c
  * mla_kv_quantize_fp8 writes them): with more than 32 query rows (s_q *
  * h_q) the pages are dequantised to bf16 values code * scale before the
  * products, which is exact for such scales (any other scale is rounded to
- * bf16 there). Errors as for mla_decode, plus MLA_ERR_NULL_ARG for
+ * bf16 there; mla_check_fp8_scales finds such scales in a cache written by
+ * other means). Errors as for mla_decode, plus MLA_ERR_NULL_ARG for
  * kv_scales = NULL and MLA_ERR_BAD_SHAPE for a misaligned kv_scales. */
 int mla_decode_fp8(const void* q, const void* kv_codes, const float* kv_scales,
                    const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
@@ -384,6 +385,20 @@ int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q
 int mla_check_pages(const int32_t* block_table, const int32_t* cache_seqlens, int32_t batch,
                     int32_t num_pages, int32_t max_pages_per_seq, int32_t* status,
                     hipStream_t stream);
+
+/* Debug check of an FP8 cache's per-token scales (the format above):
+ * mla_decode_fp8 dequantises exactly only scales that are positive normal
+ * powers of two, which is what mla_kv_quantize_fp8 writes; a cache filled
+ * by other means can be checked with this call. One workgroup reads the n
+ * fp32 scales at kv_scales and writes status int32[4] on the device:
+ * [number of scales that are not positive normal powers of two, index of
+ * the first such scale as two words (low, high; -1 when none), its fp32
+ * bits (0 when none)]. Enqueued on `stream`; nothing is synchronised, and
+ * the status needs no initialisation.
+ * Errors: MLA_ERR_NULL_ARG for status = NULL, or kv_scales = NULL with
+ * n > 0; MLA_ERR_BAD_SHAPE for n < 0 or a misaligned pointer. */
+int mla_check_fp8_scales(const float* kv_scales, int64_t n, int32_t* status,
+                         hipStream_t stream);
 
 /* Profiling hook: while set, every mla_decode / gqa_decode call records the
  * HIP event `start` on its stream right before its main decode kernel and

@@ -23,7 +23,7 @@ __all__ = ["Plan", "PlanInfo", "DecodeError", "plan_info", "mla_decode_plan", "m
            "mla_decode_noalloc",
            "gqa_decode", "attn_combine", "mla_kv_append", "gqa_kv_append",
            "mla_decode_fp8", "mla_kv_append_fp8", "mla_kv_quantize_fp8", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output", "gqla_decode",
-           "mla_decode_plan_host", "mla_check_pages", "profile_events"]
+           "mla_decode_plan_host", "mla_check_pages", "mla_check_fp8_scales", "profile_events"]
 
 MLA_D, MLA_DV = 576, 512
 GQA_D = 128
@@ -456,6 +456,20 @@ def mla_check_pages(block_table, cache_seqlens, num_pages, status=None):
     _lib.check("mla_check_pages", _lib.lib().mla_check_pages(
         _ptr(block_table), _ptr(cache_seqlens), B, int(num_pages), max_pages, _ptr(status),
         _stream()))
+    return status
+
+
+def mla_check_fp8_scales(kv_scales, status=None):
+    """Check that every per-token scale of an FP8 cache is a positive
+    normal power of two (what mla_decode_fp8 dequantises exactly).
+    kv_scales fp32 [num_pages, 64]. Returns status int32 [4] on the device,
+    filled asynchronously: [violations, first index low word, high word,
+    its fp32 bits]."""
+    _need(kv_scales, "kv_scales", torch.float32)
+    if status is None:
+        status = torch.empty(4, dtype=torch.int32, device=kv_scales.device)
+    _lib.check("mla_check_fp8_scales", _lib.lib().mla_check_fp8_scales(
+        _ptr(kv_scales), kv_scales.numel(), _ptr(status), _stream()))
     return status
 
 

@@ -47,6 +47,7 @@ _SIGS = {
     "mla_kv_quantize_fp8": [_P, _P, _P, ctypes.c_int64, _P],
     "mla_decode_plan_host": [_P, _I, _I, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PlanInfo)],
     "mla_check_pages": [_P, _P, _I, _I, _I, _P, _P],
+    "mla_check_fp8_scales": [_P, ctypes.c_int64, _P, _P],
     "mla_status_string": [ctypes.c_int],
     "mla_ceiling_mfma": [_I, _I, _I, _I, _I, _P, _P],
     "mla_ceiling_stream_read": [_P, ctypes.c_size_t, _I, _P, _P],

@@ -570,6 +570,15 @@ int mla_check_pages(const int32_t* block_table, const int32_t* cache_seqlens, in
   return MLA_OK;
 }
 
+int mla_check_fp8_scales(const float* kv_scales, int64_t n, int32_t* status, hipStream_t stream) {
+  if (!status) return MLA_ERR_NULL_ARG;
+  if (n < 0) return MLA_ERR_BAD_SHAPE;
+  if (n > 0 && !kv_scales) return MLA_ERR_NULL_ARG;
+  if (((uintptr_t)status & 3) != 0 || ((uintptr_t)kv_scales & 3) != 0) return MLA_ERR_BAD_SHAPE;
+  if (mla::launch_check_fp8_scales(kv_scales, n, status, stream) != hipSuccess) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 void mla_profile_events(void* start, void* stop) {
   g_prof_start = (hipEvent_t)start;
   g_prof_stop = (hipEvent_t)stop;

@@ -360,4 +360,60 @@ hipError_t launch_check_pages(const int32_t* block_table, const int32_t* seqlens
   return hipGetLastError();
 }
 
+// Check of an FP8 cache's per-token scales, one workgroup: a scale passes
+// when it is a positive normal power of two (sign 0, exponent field 1..254,
+// mantissa field 0), the scales mla_kv_quantize_fp8 writes and the ones the
+// 64-row decode dequantises to bf16 exactly. The workgroup counts the others
+// and keeps the smallest index among them; one thread stores [count, index
+// low word, index high word, the scale's bits], so the status needs no
+// initialisation.
+__global__ __launch_bounds__(CHECK_THREADS) void check_fp8_scales_kernel(const uint32_t* bits,
+                                                                         int64_t n,
+                                                                         int32_t* status) {
+  __shared__ int s_count[CHECK_THREADS / 64];
+  __shared__ int64_t s_first[CHECK_THREADS / 64];
+  int count = 0;
+  int64_t first = INT64_MAX;
+  for (int64_t i = threadIdx.x; i < n; i += CHECK_THREADS) {
+    const uint32_t u = bits[i];
+    const uint32_t e = (u >> 23) & 0xffu;
+    const bool ok = (u >> 31) == 0u && e >= 1u && e <= 254u && (u & 0x7fffffu) == 0u;
+    if (!ok) {
+      ++count;
+      first = first < i ? first : i;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    count += __shfl_xor(count, off);
+    const int64_t o = __shfl_xor(first, off);
+    first = first < o ? first : o;
+  }
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  if (lane == 0) {
+    s_count[wv] = count;
+    s_first[wv] = first;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = 0;
+    int64_t f = INT64_MAX;
+    for (int w = 0; w < CHECK_THREADS / 64; ++w) {
+      c += s_count[w];
+      f = f < s_first[w] ? f : s_first[w];
+    }
+    status[0] = c;
+    if (f == INT64_MAX) f = -1;
+    status[1] = (int32_t)(uint32_t)(uint64_t)f;
+    status[2] = (int32_t)(uint32_t)((uint64_t)f >> 32);
+    status[3] = f < 0 ? 0 : (int32_t)bits[f];
+  }
+}
+
+hipError_t launch_check_fp8_scales(const float* scales, int64_t n, int32_t* status,
+                                   hipStream_t st) {
+  hipLaunchKernelGGL(check_fp8_scales_kernel, dim3(1), dim3(CHECK_THREADS), 0, st,
+                     (const uint32_t*)scales, n, status);
+  return hipGetLastError();
+}
+
 }  // namespace mla

@@ -124,6 +124,8 @@ hipError_t launch_decode_kernel(const DecodeArgs& a, int nw, int kind, int grid,
 // the two launches of levels 1 and 2 when a.Z > 1).
 hipError_t launch_combine_kernel(const CombineArgs& a, hipStream_t st);
 // Device-side precondition check of the decode calls (one workgroup).
+hipError_t launch_check_fp8_scales(const float* scales, int64_t n, int32_t* status,
+                                   hipStream_t st);
 hipError_t launch_check_pages(const int32_t* block_table, const int32_t* seqlens, int B,
                               int num_pages, int max_pages, int32_t* status, hipStream_t st);
 // Schedule: signature, worker records and unit prefix into meta, slot

@@ -25,7 +25,8 @@ def test_every_declared_function_is_exported(L):
     assert {"mla_decode_plan", "mla_decode", "gqa_decode", "attn_combine", "mla_kv_append",
             "gqa_kv_append", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output",
             "gqla_decode", "mla_decode_fp8", "mla_kv_append_fp8",
-            "mla_kv_quantize_fp8", "mla_check_pages", "mla_decode_noalloc"} <= set(names)
+            "mla_kv_quantize_fp8", "mla_check_pages", "mla_decode_noalloc",
+            "mla_check_fp8_scales"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -114,6 +115,15 @@ def test_check_pages_argument_checks(L):
     assert L.mla_check_pages(p, p, 2, 0, 4, p, None) == -2
     assert L.mla_check_pages(p, p, 2, 10, 0, p, None) == -2
     assert L.mla_check_pages(p, p, 2, 10, 4, ctypes.c_void_p(66), None) == -2
+
+
+def test_check_fp8_scales_argument_checks(L):
+    p = ctypes.c_void_p(64)
+    assert L.mla_check_fp8_scales(p, 10, None, None) == -1             # no status word
+    assert L.mla_check_fp8_scales(None, 10, p, None) == -1
+    assert L.mla_check_fp8_scales(p, -1, p, None) == -2
+    assert L.mla_check_fp8_scales(ctypes.c_void_p(66), 10, p, None) == -2   # unaligned scales
+    assert L.mla_check_fp8_scales(p, 10, ctypes.c_void_p(66), None) == -2   # unaligned status
 
 
 def test_kv_append_argument_checks(L):

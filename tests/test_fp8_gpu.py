@@ -230,3 +230,47 @@ def test_fp8_decode_full_size(dev, idx):
     check(out[idx_s], lse[idx_s], ref_out, ref_lse, f"fp8 config {idx} (sampled)")
     # the GPU's codes of those pages are the oracle's
     assert np.array_equal(c.cpu().numpy()[pages], codes[pages])
+
+
+# ------------------------------------------------------------ scale check
+def _scale_status(scales, dev):
+    import torch
+    import mla_paged_kv_03_amd as lib
+    st = lib.mla_check_fp8_scales(torch.from_numpy(np.ascontiguousarray(scales)).to(dev))
+    torch.cuda.synchronize()
+    s = st.cpu().numpy().astype(np.int64)
+    first = (s[1] & 0xffffffff) | (s[2] << 32)
+    return int(s[0]), int(first), int(s[3]) & 0xffffffff
+
+
+@pytest.mark.parametrize("which", ["config1", "config3_part"])
+def test_scale_check_passes_quantised_caches(dev, which):
+    """Scales the oracle's quantiser writes are powers of two: none flagged."""
+    cfg = CONFIGS[1] if which == "config1" else CONFIGS[3].with_(batch=16)
+    kv = make_inputs(cfg)["kv"][:, :, 0, :]
+    _, scales = fp8.quantize_rows(kv.reshape(-1, 576))
+    log(f"[case] scale check {which}: {scales.size} scales")
+    assert _scale_status(scales.reshape(kv.shape[0], -1), dev) == (0, -1, 0)
+
+
+def test_scale_check_counts_planted_scales(dev):
+    """Planted scales that are not positive normal powers of two are counted,
+    and the first of them is named with its bits: 3.0 (mantissa set), -0.5
+    (sign), a subnormal, 0, +inf and NaN (exponent field 0 or 255); the
+    largest and smallest normal powers of two pass."""
+    n = 64 * 1000 + 37                       # several passes of the workgroup, ragged tail
+    scales = np.exp2(np.random.default_rng(11).integers(-20, 20, n)).astype(np.float32)
+    scales[5] = np.float32(2.0 ** 127)
+    scales[6] = np.float32(2.0 ** -126)
+    assert _scale_status(scales, dev) == (0, -1, 0)
+    planted = {777: 3.0, 1024: -0.5, 4097: np.float32(2.0 ** -130), 40000: 0.0,
+               50001: np.inf, n - 1: np.nan}
+    for i, v in planted.items():
+        scales[i] = v
+    log(f"[case] scale check: {n} scales, {len(planted)} planted")
+    assert _scale_status(scales, dev) == (len(planted), 777, int(np.float32(3.0).view(np.uint32)))
+    scales[777] = 1.0
+    assert _scale_status(scales, dev) == (len(planted) - 1, 1024,
+                                         int(np.float32(-0.5).view(np.uint32)))
+    empty = np.zeros(0, np.float32)
+    assert _scale_status(empty, dev) == (0, -1, 0)
