@@ -83,6 +83,33 @@ __device__ __forceinline__ void scores_ready(f32x16& s0, f32x16& s1) {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// Scalar loads from wave-uniform addresses, issued together and waited for
+// in the same statement: one memory round trip for all of them. The block
+// opens with one wait state after a possible VALU write of the address
+// registers; the results are early-clobber, so no result register doubles as
+// an address still to be read.
+__device__ __forceinline__ void sload6(const int32_t* p, int (&v)[6]) {
+  int a0, a1, a2, a3, a4, a5;
+  asm volatile(
+      "s_nop 0\n\ts_load_dword %0, %6, 0x0\n\ts_load_dword %1, %6, 0x4\n\t"
+      "s_load_dword %2, %6, 0x8\n\ts_load_dword %3, %6, 0xc\n\ts_load_dword %4, %6, 0x10\n\t"
+      "s_load_dword %5, %6, 0x14\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(a0), "=&s"(a1), "=&s"(a2), "=&s"(a3), "=&s"(a4), "=&s"(a5)
+      : "s"(p)
+      : "memory");
+  v[0] = a0; v[1] = a1; v[2] = a2; v[3] = a3; v[4] = a4; v[5] = a5;
+}
+// *p, *q and *(q + 1) in one round trip
+__device__ __forceinline__ void sload_1_2(const int32_t* p, const int32_t* q, int& x, int& y0,
+                                          int& y1) {
+  asm volatile(
+      "s_nop 0\n\ts_load_dword %0, %3, 0x0\n\ts_load_dword %1, %4, 0x0\n\t"
+      "s_load_dword %2, %4, 0x4\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(x), "=&s"(y0), "=&s"(y1)
+      : "s"(p), "s"(q)
+      : "memory");
+}
+
 // Raw buffer descriptor of n bytes from p (no stride, 32-bit data format):
 // loads at offsets >= n return zeros and read no memory.
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t n) {
@@ -135,13 +162,18 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
     return;
   // wave-uniform values come in by scalar loads
   const int32_t* rec = uniform_ptr(sched::records(a.meta) + w * sched::REC);
-  const int bs = sload(rec + sched::R_B_START);
-  const int be = sload(rec + sched::R_B_END);
+  static_assert(sched::R_B_START < 6 && sched::R_B_END < 6 && sched::R_OWNS_FIRST < 6 &&
+                    sched::R_SPLIT0 < 6 && sched::R_P_START < 6 && sched::R_P_END < 6,
+                "the record words read here are its first six");
+  int rw[6];
+  sload6(rec, rw);
+  const int bs = rw[sched::R_B_START];
+  const int be = rw[sched::R_B_END];
   if (be < bs) return;
-  const int owns_first = sload(rec + sched::R_OWNS_FIRST);
-  const int split0 = sload(rec + sched::R_SPLIT0);
-  const int p_start = sload(rec + sched::R_P_START);
-  const int p_end = sload(rec + sched::R_P_END);
+  const int owns_first = rw[sched::R_OWNS_FIRST];
+  const int split0 = rw[sched::R_SPLIT0];
+  const int p_start = rw[sched::R_P_START];
+  const int p_end = rw[sched::R_P_END];
 
   const int TH = a.T * a.H;
   const bool scale_neg = a.scale_log2 < 0.f;
@@ -200,15 +232,15 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
   const int32_t* seqlens = uniform_ptr(a.seqlens);
   const int32_t* slots = uniform_ptr(a.slots);
   for (int b = bs; b <= be; ++b) {
-    const int L = sload(seqlens + b);
+    int L, s0, s1;
+    sload_1_2(seqlens + b, slots + b, L, s0, s1);
     const int npg = sched::seq_pages(L);
     // the page range of schedule.h's page_range, from the record's words
     int p0 = b == bs ? p_start : 0;
     int p1 = b == be ? p_end : npg;
     p1 = min(p1, npg);
     p0 = max(p0, 0);
-    const int s0 = sload(slots + b);
-    const int nslots = sload(slots + b + 1) - s0;
+    const int nslots = s1 - s0;
 
     if (npg == 0) {
       if ((b > bs || owns_first) && row_ok) {
