@@ -540,20 +540,8 @@ int mla_decode_plan_host(const int32_t* seqlens_host, int32_t batch, int32_t s_q
   if (!sched_metadata_host && !num_splits_host) return MLA_OK;
   if (!sched_metadata_host || !num_splits_host || (batch > 0 && !seqlens_host))
     return MLA_ERR_NULL_ARG;
-  sched::write_header(sched_metadata_host, g.W, batch, g.TH, g.G, g.DV, g.fix);
-  int32_t* prefix = sched::unit_prefix(sched_metadata_host, g.W);
-  prefix[0] = 0;
-  for (int b = 0; b < batch; ++b)
-    prefix[b + 1] = prefix[b] + sched::seq_units(seqlens_host[b], g.fix);
-  for (int w = 0; w < g.W; ++w)
-    sched::worker_record(w, g.W, prefix, seqlens_host, batch, g.fix,
-                         sched::records(sched_metadata_host) + (size_t)w * sched::REC);
-  int32_t acc = 0;
-  for (int b = 0; b < batch; ++b) {
-    num_splits_host[b] = acc;
-    acc += sched::seq_slots(b, g.W, prefix, seqlens_host, batch, g.fix);
-  }
-  num_splits_host[batch] = acc;
+  sched::host_plan(seqlens_host, batch, g.W, g.TH, g.G, g.DV, g.fix, sched_metadata_host,
+                   num_splits_host);
   return MLA_OK;
 }
 

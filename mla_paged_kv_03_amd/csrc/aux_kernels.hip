@@ -47,7 +47,7 @@ constexpr int PLAN_LDS_SEQS = 8192;
 
 // One workgroup. Writes the plan's signature, the unit prefix (B + 1 entries
 // after the W worker records), every worker record, and the exclusive prefix
-// of partial slots (B + 1 entries).
+// of partial slots (B + 1 entries): schedule.h's host_plan, in parallel.
 __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqlens, int B, int W,
                                                            int rows, int G, int DV, int fix,
                                                            int32_t* meta, int32_t* slots) {
@@ -58,33 +58,40 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
   int32_t* prefix = sched::unit_prefix(meta, W);
   const bool in_lds = B <= PLAN_LDS_SEQS;
 
-  int carry = 0, total = 0;
-  if (tid == 0) {
-    sched::write_header(meta, W, B, rows, G, DV, fix);
-    prefix[0] = 0;
-    s_prefix[0] = 0;
-  }
+  // step 1: the batch's cost T, each sequence taken whole
+  int T = 0, total = 0;
   for (int base = 0; base < B; base += PLAN_THREADS) {
     const int b = base + tid;
     const int L = b < B ? seqlens[b] : 0;
-    const int v = b < B ? sched::seq_units(L, fix) : 0;
+    block_scan(b < B ? sched::seq_cost(L, fix) : 0, buf, &total);
+    if (b < B && in_lds) s_len[b] = L;
+    T += total;
+  }
+  if (tid == 0) {
+    sched::write_header(meta, W, B, rows, G, DV, fix, T);
+    prefix[0] = 0;
+    s_prefix[0] = 0;
+  }
+  __syncthreads();
+  const int32_t* len = in_lds ? s_len : seqlens;
+  // step 2: the line of blocks and its prefix
+  int carry = 0;
+  for (int base = 0; base < B; base += PLAN_THREADS) {
+    const int b = base + tid;
+    const int v = b < B ? sched::seq_units(len[b], fix, T, W) : 0;
     const int inc = block_scan(v, buf, &total);
     if (b < B) {
       prefix[b + 1] = carry + inc;
-      if (in_lds) {
-        s_prefix[b + 1] = carry + inc;
-        s_len[b] = L;
-      }
+      if (in_lds) s_prefix[b + 1] = carry + inc;
     }
     carry += total;
   }
   __threadfence_block();
   __syncthreads();
   const int32_t* pre = in_lds ? s_prefix : prefix;
-  const int32_t* len = in_lds ? s_len : seqlens;
 
   for (int w = tid; w < W; w += PLAN_THREADS)
-    sched::worker_record(w, W, pre, len, B, fix, sched::records(meta) + (size_t)w * sched::REC);
+    sched::worker_record(w, W, pre, len, B, fix, T, sched::records(meta) + (size_t)w * sched::REC);
 
   carry = 0;
   for (int base = 0; base < B; base += PLAN_THREADS) {

@@ -3,15 +3,25 @@
 //
 // FlashAttention (KO), section "FlashAttention-2 (2023)", credits better
 // parallelism and work partitioning across the GPU; the FlashMLA blog
-// ("기술 기반") asks for efficient variable-length handling. Here the work
-// of sequence b is `fix` overhead units (loading its queries, writing its
-// result) followed by one unit per 64-token page; the units of the whole
-// batch are concatenated and cut into num_workers equal contiguous ranges of
-// `chunk` units. A sequence whose pages fall into several ranges is split;
-// each piece writes a partial result that a log-sum-exp merge finishes.
-// `fix` is part of the plan (FIX_LATENT128 for the 128-row latent decode,
-// whose per-sequence queries and output weigh several pages, FIX_DEFAULT
-// otherwise) and is recorded in the plan's signature.
+// ("기술 기반") asks for efficient variable-length handling. A worker pays
+// `fix` overhead units (loading the queries, writing the result) for every
+// piece of a sequence it processes, and one unit per 64-token page. The plan:
+//   1. Sequence b costs p_b + fix units if one worker takes it whole; with
+//      T the batch's total of that cost, it is cut into
+//      k_b = clamp(round((p_b + fix) * W / T), 1, p_b) pieces: its share
+//      of the W workers.
+//   2. Sequence b is laid out as k_b blocks, each `fix` overhead units
+//      followed by its pages (the first p_b % k_b blocks one page more than
+//      the others); the blocks of the whole batch are concatenated and the
+//      line is cut into W equal contiguous ranges of `chunk` units.
+// So a worker that starts a piece of a split sequence finds that piece's
+// overhead at the start of its range, and a batch of equal sequences splits
+// into equal pieces exactly on the block boundaries. A sequence whose pages
+// fall into several ranges is split; each piece writes a partial result
+// that a log-sum-exp merge finishes. `fix` is part of the plan
+// (FIX_LATENT128 for the 128-row latent decode, whose queries and output
+// weigh several pages, FIX_DEFAULT otherwise) and is recorded in the plan's
+// signature, with T.
 //
 // Every function here is plain arithmetic usable on the host (for the
 // host-side checker) and on the device (for the plan kernel).
@@ -40,9 +50,10 @@ constexpr int REC = 8;  // int32 per worker record
 // value width is passed in.
 constexpr int HDR = 8;
 constexpr int32_t PLAN_MAGIC = 0x4D4C4150;  // "PALM" in memory order
-enum : int { H_MAGIC = 0, H_W = 1, H_B = 2, H_ROWS = 3, H_G = 4, H_DV = 5, H_FIX = 6 };
+enum : int { H_MAGIC = 0, H_W = 1, H_B = 2, H_ROWS = 3, H_G = 4, H_DV = 5, H_FIX = 6, H_COST = 7 };
 
-SCHED_HD void write_header(int32_t* hdr, int W, int B, int rows, int G, int DV, int fix) {
+SCHED_HD void write_header(int32_t* hdr, int W, int B, int rows, int G, int DV, int fix,
+                           int32_t cost) {
   hdr[H_MAGIC] = PLAN_MAGIC;
   hdr[H_W] = W;
   hdr[H_B] = B;
@@ -50,7 +61,7 @@ SCHED_HD void write_header(int32_t* hdr, int W, int B, int rows, int G, int DV, 
   hdr[H_G] = G;
   hdr[H_DV] = DV;
   hdr[H_FIX] = fix;
-  hdr[7] = 0;
+  hdr[H_COST] = cost;
 }
 
 // Records of the workers, and the unit prefix, inside the metadata.
@@ -71,7 +82,46 @@ enum : int {
 };
 
 SCHED_HD int seq_pages(int32_t L) { return L > 0 ? (L + PAGE - 1) / PAGE : 0; }
-SCHED_HD int seq_units(int32_t L, int fix) { return seq_pages(L) + fix; }
+// cost of sequence b taken whole (step 1); T is their sum over the batch
+SCHED_HD int seq_cost(int32_t L, int fix) { return seq_pages(L) + fix; }
+// number of pieces (blocks) of a sequence: its share of the workers, at
+// least one and at most one per page
+SCHED_HD int seq_pieces(int32_t L, int fix, int32_t T, int W) {
+  const int p = seq_pages(L);
+  if (p == 0 || T <= 0) return 1;
+  int64_t k = (2 * (int64_t)seq_cost(L, fix) * W + T) / (2 * (int64_t)T);
+  if (k < 1) k = 1;
+  if (k > p) k = p;
+  return (int)k;
+}
+// units of a sequence on the line (step 2): every block's overhead and pages
+SCHED_HD int seq_units(int32_t L, int fix, int32_t T, int W) {
+  const int p = seq_pages(L);
+  return p + fix * seq_pieces(L, fix, T, W);
+}
+// Pages of a sequence that lie before its unit offset x (0 <= x <= units):
+// the overhead units of a block count as lying before the block's pages.
+SCHED_HD int pages_before(int32_t L, int fix, int32_t T, int W, int64_t x) {
+  const int p = seq_pages(L);
+  if (p == 0) return 0;
+  const int n = seq_pieces(L, fix, T, W);
+  const int q = p / n, r = p % n;  // blocks 0 .. r - 1 hold q + 1 pages, the rest q
+  const int64_t big = fix + q + 1, small = fix + q, xr = (int64_t)r * big;
+  int64_t i, off, before;
+  if (x < xr) {
+    i = x / big;
+    off = x - i * big;
+    before = i * (q + 1);
+  } else {
+    i = r + (x - xr) / small;
+    off = (x - xr) - (i - r) * small;
+    before = (int64_t)r * (q + 1) + (i - r) * q;
+  }
+  if (i >= n) return p;
+  const int64_t bp = i < r ? q + 1 : q;
+  const int64_t in = off - fix;
+  return (int)(before + (in < 0 ? 0 : (in > bp ? bp : in)));
+}
 
 // Largest b in [0, B) with prefix[b] <= u (prefix strictly increasing,
 // prefix[0] = 0 <= u).
@@ -84,16 +134,19 @@ SCHED_HD int find_seq(const int32_t* prefix, int B, int64_t u) {
   return lo;
 }
 
-SCHED_HD int chunk_units(int32_t total_units, int W) {
-  int c = (total_units + W - 1) / W;
-  return c > 0 ? c : 1;
+// Units per worker: at least one more than a block's overhead, so that a
+// range inside a split sequence always holds one of its pages.
+SCHED_HD int chunk_units(int32_t total_units, int W, int fix) {
+  const int c = (total_units + W - 1) / W;
+  return c > fix ? c : fix + 1;
 }
 
-// Record of worker w. prefix has B + 1 entries (prefix[B] = total units).
+// Record of worker w. prefix has B + 1 entries (prefix[B] = total units of
+// the line); T is the batch's cost from step 1.
 SCHED_HD void worker_record(int w, int W, const int32_t* prefix, const int32_t* seqlens,
-                            int B, int fix, int32_t* rec) {
+                            int B, int fix, int32_t T, int32_t* rec) {
   const int32_t C = prefix[B];
-  const int chunk = chunk_units(C, W);
+  const int chunk = chunk_units(C, W, fix);
   const int64_t lo = (int64_t)w * chunk;
   if (lo >= C) {
     rec[R_B_START] = 0; rec[R_P_START] = 0; rec[R_B_END] = -1; rec[R_P_END] = 0;
@@ -103,17 +156,15 @@ SCHED_HD void worker_record(int w, int W, const int32_t* prefix, const int32_t* 
   const int64_t hi = (lo + chunk < C) ? lo + chunk : C;
   const int bs = find_seq(prefix, B, lo);
   const int be = find_seq(prefix, B, hi - 1);
-  int64_t ps = lo - prefix[bs] - fix;
-  if (ps < 0) ps = 0;
-  const int ne = seq_pages(seqlens[be]);
-  int64_t pe = hi - prefix[be] - fix;
-  if (pe < 0) pe = 0;
-  if (pe > ne) pe = ne;
+  const int ps = pages_before(seqlens[bs], fix, T, W, lo - prefix[bs]);
+  const int pe = pages_before(seqlens[be], fix, T, W, hi - prefix[be]);
+  // the worker holding the sequence's first page (its first block opens
+  // with the overhead units)
   const int first_w = (prefix[bs] + fix) / chunk;
   rec[R_B_START] = bs;
-  rec[R_P_START] = (int32_t)ps;
+  rec[R_P_START] = ps;
   rec[R_B_END] = be;
-  rec[R_P_END] = (int32_t)pe;
+  rec[R_P_END] = pe;
   rec[R_SPLIT0] = w > first_w ? w - first_w : 0;
   rec[R_OWNS_FIRST] = prefix[bs] == lo ? 1 : 0;
   rec[R_LO] = (int32_t)lo;
@@ -134,11 +185,14 @@ SCHED_HD void page_range(const int32_t* rec, int b, int bs, int be, int npg, int
   *p1 = hi;
 }
 
-// Number of workers that process pages of sequence b (1 for an empty one).
+// Number of workers that process pages of sequence b (1 for an empty one):
+// those holding its first page, its last unit (a page: every block ends with
+// pages) and every range between, each of which holds a page since a range
+// is longer than a block's overhead.
 SCHED_HD int seq_split_count(int b, int W, const int32_t* prefix, const int32_t* seqlens, int B,
                              int fix) {
   if (seq_pages(seqlens[b]) == 0) return 1;
-  const int chunk = chunk_units(prefix[B], W);
+  const int chunk = chunk_units(prefix[B], W, fix);
   const int first = (prefix[b] + fix) / chunk;
   const int last = (prefix[b + 1] - 1) / chunk;
   return last - first + 1;
@@ -149,6 +203,26 @@ SCHED_HD int seq_slots(int b, int W, const int32_t* prefix, const int32_t* seqle
                        int fix) {
   const int n = seq_split_count(b, W, prefix, seqlens, B, fix);
   return n > 1 ? n : 0;
+}
+
+// The whole plan on the host, in the order the plan kernel computes it:
+// header, prefix of line units, worker records, slot prefix (B + 1 entries).
+inline void host_plan(const int32_t* seqlens, int B, int W, int rows, int G, int DV, int fix,
+                      int32_t* meta, int32_t* splits) {
+  int64_t T = 0;
+  for (int b = 0; b < B; ++b) T += seq_cost(seqlens[b], fix);
+  write_header(meta, W, B, rows, G, DV, fix, (int32_t)T);
+  int32_t* prefix = unit_prefix(meta, W);
+  prefix[0] = 0;
+  for (int b = 0; b < B; ++b) prefix[b + 1] = prefix[b] + seq_units(seqlens[b], fix, (int32_t)T, W);
+  for (int w = 0; w < W; ++w)
+    worker_record(w, W, prefix, seqlens, B, fix, (int32_t)T, records(meta) + (size_t)w * REC);
+  int32_t acc = 0;
+  for (int b = 0; b < B; ++b) {
+    splits[b] = acc;
+    acc += seq_slots(b, W, prefix, seqlens, B, fix);
+  }
+  splits[B] = acc;
 }
 
 }  // namespace sched

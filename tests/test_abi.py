@@ -252,24 +252,67 @@ def test_schedule_covers_every_page_once(seqlens, shape, cus):
     assert sorted(slot_users) == list(range(splits[-1]))
     for b in range(len(seqlens)):
         assert splits[b + 1] - splits[b] != 1, "a single piece never uses a slot"
-    # the prefix of work units follows the per-sequence cost: its pages and
-    # the plan's overhead units, recorded in the signature (more for the
-    # 128-row latent decode, whose queries and output weigh several pages)
+    # the line: each sequence is k blocks of `fix` overhead units and its
+    # pages, k its share of the workers by cost (pages + fix), recorded
+    # total T in the signature; fix is more for the 128-row latent decode,
+    # whose queries and output weigh several pages
     fix = int(meta[6])
     assert fix == (FIX_LATENT128 if (G == 1 and dv == 512 and T * H >= 128) else FIX_DEFAULT)
+    pages = [(int(L) + 63) // 64 for L in seqlens]
+    cost = sum(p + fix for p in pages)
+    assert int(meta[7]) == cost
     units = meta[HDR + W * REC:HDR + W * REC + len(seqlens) + 1]
-    expect = np.concatenate([[0], np.cumsum([(int(L) + 63) // 64 + fix for L in seqlens])])
-    assert np.array_equal(units, expect)
+    assert units[0] == 0
+    for b, p in enumerate(pages):
+        k = (units[b + 1] - units[b] - p) // fix
+        assert units[b + 1] - units[b] == p + k * fix
+        share = (2 * (p + fix) * W + cost) // (2 * cost) if cost else 1
+        assert k == (1 if p == 0 else min(max(share, 1), p))
 
 
-def test_schedule_balances_work():
-    seqlens = list(np.random.default_rng(3).integers(1, 16385, size=128))
+def _worker_costs(seqlens, meta, info):
+    """Per worker: pages processed plus the overhead units of every piece."""
+    W, fix = info.num_workers, int(meta[6])
+    pages = [(int(L) + 63) // 64 for L in seqlens]
+    costs = []
+    for w in range(W):
+        bs, ps, be, pe = meta[HDR + w * REC:HDR + w * REC + 4]
+        c = 0
+        for b in range(bs, be + 1):
+            p0 = ps if b == bs else 0
+            p1 = min(pe if b == be else pages[b], pages[b])
+            if p1 > p0:
+                c += p1 - p0 + fix
+        costs.append(c)
+    return costs
+
+
+@pytest.mark.parametrize("seqlens", SCHEDULES + [
+    list(np.random.default_rng(3).integers(1, 16385, size=128))])
+def test_schedule_balances_work(seqlens):
+    """Every worker's range is one chunk of the line; a worker pays at most
+    one piece's overhead beyond the units in its range (when it starts a
+    piece in the middle of a block)."""
     meta, splits, info = mla_decode_plan_host(seqlens, 2, 128, num_cus=256)
-    W = info.num_workers
+    W, fix = info.num_workers, int(meta[6])
     loads = [meta[HDR + w * REC + 7] - meta[HDR + w * REC + 6] for w in range(W)]
-    total = sum((int(L) + 63) // 64 + int(meta[6]) for L in seqlens)
-    chunk = -(-total // W)
+    total = int(meta[HDR + W * REC + len(seqlens)])
+    chunk = max(-(-total // W), fix + 1)
     assert max(loads) <= chunk and sum(loads) == total
+    assert max(_worker_costs(seqlens, meta, info)) <= chunk + fix
+
+
+def test_equal_sequences_split_into_equal_pieces():
+    """The DeepSeek-V3 decode batch (64 sequences of 4096 tokens, 128 heads)
+    on 256 workers: every worker gets one piece of 16 pages."""
+    seqlens = [4096] * 64
+    meta, splits, info = mla_decode_plan_host(seqlens, 1, 128, num_cus=256)
+    W = info.num_workers
+    assert W == 256
+    for w in range(W):
+        bs, ps, be, pe = meta[HDR + w * REC:HDR + w * REC + 4]
+        assert bs == be and pe - ps == 16, (w, bs, ps, be, pe)
+    assert list(np.diff(splits)) == [4] * 64
 
 
 def test_workspace_size_matches_slot_bound():
@@ -292,7 +335,8 @@ def test_plan_opens_with_its_geometry(shape):
     assert info.metadata_bytes == 4 * (HDR + info.num_workers * REC + len(seqlens) + 1)
     assert list(meta[:6]) == [0x4D4C4150, info.num_workers, len(seqlens), T * H, G, dv]
     fix = FIX_LATENT128 if (G == 1 and dv == 512 and T * H >= 128) else FIX_DEFAULT
-    assert list(meta[6:8]) == [fix, 0]
+    cost = sum((L + 63) // 64 + fix for L in seqlens)
+    assert list(meta[6:8]) == [fix, cost]
 
 
 def test_page_range_is_clamped_to_current_lengths(tmp_path):
@@ -318,13 +362,11 @@ int main(int argc, char** argv) {
   const int B = (argc - 2) / 2;
   std::vector<int32_t> Lp(B), Lc(B), meta(sched::HDR + W * sched::REC + B + 1);
   for (int b = 0; b < B; ++b) { Lp[b] = atoi(argv[2 + b]); Lc[b] = atoi(argv[2 + B + b]); }
-  int32_t* prefix = sched::unit_prefix(meta.data(), W);
-  prefix[0] = 0;
-  for (int b = 0; b < B; ++b) prefix[b + 1] = prefix[b] + sched::seq_units(Lp[b], FIX);
+  std::vector<int32_t> splits(B + 1);
+  sched::host_plan(Lp.data(), B, W, 128, 1, 512, FIX, meta.data(), splits.data());
   long pairs = 0;
   for (int w = 0; w < W; ++w) {
     int32_t* rec = sched::records(meta.data()) + w * sched::REC;
-    sched::worker_record(w, W, prefix, Lp.data(), B, FIX, rec);
     for (int b = rec[sched::R_B_START]; b <= rec[sched::R_B_END]; ++b) {
       const int npg = sched::seq_pages(Lc[b]);
       int p0, p1;
