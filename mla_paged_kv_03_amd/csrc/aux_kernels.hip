@@ -6,12 +6,12 @@
 
 namespace mla {
 
-constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_THREADS = 256;
 
 // Inclusive scan of one value per thread over the block; *total gets the
 // sum of all values. Each wave scans its 64 values with lane shuffles, wave
-// 0 scans the 16 wave totals: three barriers instead of two per doubling
-// step over the whole block.
+// 0 scans the wave totals: three barriers instead of two per doubling step
+// over the whole block.
 constexpr int PLAN_WAVES = PLAN_THREADS / 64;
 
 __device__ int block_scan(int v, int* wsum, int* total) {
@@ -58,21 +58,29 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
   int32_t* prefix = sched::unit_prefix(meta, W);
   const bool in_lds = B <= PLAN_LDS_SEQS;
 
-  // step 1: the batch's cost T, each sequence taken whole
-  int T = 0, total = 0;
-  for (int base = 0; base < B; base += PLAN_THREADS) {
-    const int b = base + tid;
-    const int L = b < B ? seqlens[b] : 0;
-    block_scan(b < B ? sched::seq_cost(L, fix) : 0, buf, &total);
-    if (b < B && in_lds) s_len[b] = L;
-    T += total;
+  // step 1: the batch's cost T, each sequence taken whole: per-thread sums,
+  // a wave reduction, one barrier
+  __shared__ int s_red[PLAN_WAVES];
+  int part = 0;
+  for (int b = tid; b < B; b += PLAN_THREADS) {
+    const int L = seqlens[b];
+    part += sched::seq_cost(L, fix);
+    if (in_lds) s_len[b] = L;
   }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+  if ((tid & 63) == 0) s_red[tid >> 6] = part;
+  __syncthreads();
+  int T = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < PLAN_WAVES; ++i) T += s_red[i];
   if (tid == 0) {
     sched::write_header(meta, W, B, rows, G, DV, fix, T);
     prefix[0] = 0;
     s_prefix[0] = 0;
   }
-  __syncthreads();
+  // (each thread reads back only the lengths it stored itself until the
+  // scan's barriers)
   const int32_t* len = in_lds ? s_len : seqlens;
   // step 2: the line of blocks and its prefix
   int carry = 0;

@@ -89,10 +89,13 @@ SCHED_HD int seq_cost(int32_t L, int fix) { return seq_pages(L) + fix; }
 SCHED_HD int seq_pieces(int32_t L, int fix, int32_t T, int W) {
   const int p = seq_pages(L);
   if (p == 0 || T <= 0) return 1;
-  int64_t k = (2 * (int64_t)seq_cost(L, fix) * W + T) / (2 * (int64_t)T);
-  if (k < 1) k = 1;
-  if (k > p) k = p;
-  return (int)k;
+  // round(cost * W / T); in 32-bit arithmetic whenever it fits (a 64-bit
+  // division is far slower on the GPU; both give the same quotient)
+  const uint64_t num = 2 * (uint64_t)seq_cost(L, fix) * (uint64_t)W + (uint64_t)T;
+  const uint64_t den = 2 * (uint64_t)T;
+  const uint64_t k = (num >> 32) == 0 && (den >> 32) == 0 ? (uint32_t)num / (uint32_t)den
+                                                          : num / den;
+  return k < 1 ? 1 : (k > (uint64_t)p ? p : (int)k);
 }
 // units of a sequence on the line (step 2): every block's overhead and pages
 SCHED_HD int seq_units(int32_t L, int fix, int32_t T, int W) {
@@ -101,13 +104,14 @@ SCHED_HD int seq_units(int32_t L, int fix, int32_t T, int W) {
 }
 // Pages of a sequence that lie before its unit offset x (0 <= x <= units):
 // the overhead units of a block count as lying before the block's pages.
-SCHED_HD int pages_before(int32_t L, int fix, int32_t T, int W, int64_t x) {
+// (All in 32 bits: a sequence's units, like the whole line, fit in int32.)
+SCHED_HD int pages_before(int32_t L, int fix, int32_t T, int W, int32_t x) {
   const int p = seq_pages(L);
   if (p == 0) return 0;
   const int n = seq_pieces(L, fix, T, W);
   const int q = p / n, r = p % n;  // blocks 0 .. r - 1 hold q + 1 pages, the rest q
-  const int64_t big = fix + q + 1, small = fix + q, xr = (int64_t)r * big;
-  int64_t i, off, before;
+  const int big = fix + q + 1, small = fix + q, xr = r * big;
+  int i, off, before;
   if (x < xr) {
     i = x / big;
     off = x - i * big;
@@ -115,12 +119,12 @@ SCHED_HD int pages_before(int32_t L, int fix, int32_t T, int W, int64_t x) {
   } else {
     i = r + (x - xr) / small;
     off = (x - xr) - (i - r) * small;
-    before = (int64_t)r * (q + 1) + (i - r) * q;
+    before = r * (q + 1) + (i - r) * q;
   }
   if (i >= n) return p;
-  const int64_t bp = i < r ? q + 1 : q;
-  const int64_t in = off - fix;
-  return (int)(before + (in < 0 ? 0 : (in > bp ? bp : in)));
+  const int bp = i < r ? q + 1 : q;
+  const int in = off - fix;
+  return before + (in < 0 ? 0 : (in > bp ? bp : in));
 }
 
 // Largest b in [0, B) with prefix[b] <= u (prefix strictly increasing,
@@ -156,8 +160,8 @@ SCHED_HD void worker_record(int w, int W, const int32_t* prefix, const int32_t* 
   const int64_t hi = (lo + chunk < C) ? lo + chunk : C;
   const int bs = find_seq(prefix, B, lo);
   const int be = find_seq(prefix, B, hi - 1);
-  const int ps = pages_before(seqlens[bs], fix, T, W, lo - prefix[bs]);
-  const int pe = pages_before(seqlens[be], fix, T, W, hi - prefix[be]);
+  const int ps = pages_before(seqlens[bs], fix, T, W, (int32_t)(lo - prefix[bs]));
+  const int pe = pages_before(seqlens[be], fix, T, W, (int32_t)(hi - prefix[be]));
   // the worker holding the sequence's first page (its first block opens
   // with the overhead units)
   const int first_w = (prefix[bs] + fix) / chunk;
