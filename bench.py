@@ -574,7 +574,7 @@ def main():
     work = algorithmic_work(d0, fp8)
     B, T, H, G = cfg.batch, cfg.s_q, cfg.h_q, cfg.h_kv
     dv = cfg.d_v
-    plan = lib.mla_decode_plan(sets[0][1]["sl"], T, H, G, dv)
+    plan = lib.mla_decode_plan(sets[0][1]["sl"], T, H, G, dv, kv_fp8=fp8)
     info = plan.info
     out = torch.empty(B, T, H, dv, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(B, T, H, dtype=torch.float32, device=dev)
@@ -585,8 +585,12 @@ def main():
 
     def step(i):
         _, t = sets[i % len(sets)]
-        rc = L.mla_decode_plan(P(t["sl"]), B, T, H, G, dv, P(plan.sched_metadata),
-                               P(plan.num_splits), pinfo, stream)
+        if fp8:
+            rc = L.mla_decode_plan_fp8(P(t["sl"]), B, T, H, P(plan.sched_metadata),
+                                       P(plan.num_splits), pinfo, stream)
+        else:
+            rc = L.mla_decode_plan(P(t["sl"]), B, T, H, G, dv, P(plan.sched_metadata),
+                                   P(plan.num_splits), pinfo, stream)
         if rc:
             raise lib.DecodeError("mla_decode_plan", rc)
         if fp8:

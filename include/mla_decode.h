@@ -115,6 +115,19 @@ int mla_decode_plan(const int32_t* cache_seqlens, int32_t batch, int32_t s_q,
                     int32_t* sched_metadata, int32_t* num_splits,
                     mla_plan_info* info, hipStream_t stream);
 
+/* The plan for mla_decode_fp8 (h_kv = 1, head_dim_v = 512), otherwise as
+ * mla_decode_plan. The FP8 decode holds 64 query rows per workgroup at any
+ * row count. From 128 rows per KV head on (s_q * h_q >= 128) its plan
+ * therefore has one worker per CU and row block of 64 (a worker's pages are
+ * taken by one workgroup per row block), where mla_decode_plan plans one
+ * worker of 128 rows per CU for the bf16 decode; below 128 rows the two
+ * plans are the same. From 128 rows on, a plan from the other call fails
+ * the decode's signature check (out and lse are left unwritten, as for any
+ * mismatched plan). */
+int mla_decode_plan_fp8(const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                        int32_t* sched_metadata, int32_t* num_splits, mla_plan_info* info,
+                        hipStream_t stream);
+
 /* MLA decode, MQA-absorb path (GQLA review, "1. Key Terms & Definitions").
  *
  *   q              bf16 [batch, s_q, h_q, 576]
@@ -249,9 +262,9 @@ int gqa_kv_append(const void* new_k, const void* new_v, void* k_cache, void* v_c
  */
 
 /* MLA decode over an FP8 latent cache: as mla_decode, with V = the first
- * 512 dequantised columns. The plan comes from mla_decode_plan with h_kv = 1
- * and head_dim_v = 512. The scales are expected to be powers of two (as
- * mla_kv_quantize_fp8 writes them): with more than 32 query rows (s_q *
+ * 512 dequantised columns. The plan comes from mla_decode_plan_fp8. The
+ * scales are expected to be powers of two (as mla_kv_quantize_fp8 writes
+ * them): with more than 32 query rows (s_q *
  * h_q) the pages are dequantised to bf16 values code * scale before the
  * products, which is exact for such scales (any other scale is rounded to
  * bf16 there; mla_check_fp8_scales finds such scales in a cache written by

@@ -59,32 +59,42 @@ class Plan:
     num_splits: torch.Tensor
     info: PlanInfo
     workspace: torch.Tensor | None
-    shape: tuple  # (batch, s_q, h_q, h_kv, head_dim_v)
+    shape: tuple  # (batch, s_q, h_q, h_kv, head_dim_v, kv_fp8)
 
 
-def plan_info(batch, s_q, h_q, h_kv=1, head_dim_v=MLA_DV) -> PlanInfo:
+def _plan_call(fp8, seqlens, batch, s_q, h_q, h_kv, head_dim_v, meta, splits, info, stream):
+    if fp8:
+        if h_kv != 1 or head_dim_v != MLA_DV:
+            raise ValueError("an FP8 cache plan is for h_kv = 1 and head_dim_v = 512")
+        return "mla_decode_plan_fp8", _lib.lib().mla_decode_plan_fp8(
+            seqlens, batch, s_q, h_q, meta, splits, ctypes.byref(info), stream)
+    return "mla_decode_plan", _lib.lib().mla_decode_plan(
+        seqlens, batch, s_q, h_q, h_kv, head_dim_v, meta, splits, ctypes.byref(info), stream)
+
+
+def plan_info(batch, s_q, h_q, h_kv=1, head_dim_v=MLA_DV, kv_fp8=False) -> PlanInfo:
     """Buffer sizes of a plan on the current device (no device work)."""
     info = PlanInfo()
-    _lib.check("mla_decode_plan", _lib.lib().mla_decode_plan(
-        None, batch, s_q, h_q, h_kv, head_dim_v, None, None, ctypes.byref(info), None))
+    _lib.check(*_plan_call(kv_fp8, None, batch, s_q, h_q, h_kv, head_dim_v, None, None, info,
+                           None))
     return info
 
 
-def mla_decode_plan(cache_seqlens, s_q, h_q, h_kv=1, head_dim_v=MLA_DV) -> Plan:
+def mla_decode_plan(cache_seqlens, s_q, h_q, h_kv=1, head_dim_v=MLA_DV, kv_fp8=False) -> Plan:
     """Allocate the plan's buffers (metadata, num_splits, workspace) and
-    enqueue the plan kernel on the current stream."""
+    enqueue the plan kernel on the current stream. kv_fp8: the plan of
+    mla_decode_fp8 (C: mla_decode_plan_fp8)."""
     _need(cache_seqlens, "cache_seqlens", torch.int32, 1)
     batch = cache_seqlens.shape[0]
-    info = plan_info(batch, s_q, h_q, h_kv, head_dim_v)
+    info = plan_info(batch, s_q, h_q, h_kv, head_dim_v, kv_fp8)
     dev = cache_seqlens.device
     meta = torch.empty(info.metadata_bytes // 4, dtype=torch.int32, device=dev)
     splits = torch.empty(batch + 1, dtype=torch.int32, device=dev)
     ws = (torch.empty(info.workspace_bytes // 4 + 64, dtype=torch.float32, device=dev)
           if info.workspace_bytes else None)
-    _lib.check("mla_decode_plan", _lib.lib().mla_decode_plan(
-        _ptr(cache_seqlens), batch, s_q, h_q, h_kv, head_dim_v, _ptr(meta), _ptr(splits),
-        ctypes.byref(info), _stream()))
-    return Plan(meta, splits, info, ws, (batch, s_q, h_q, h_kv, head_dim_v))
+    _lib.check(*_plan_call(kv_fp8, _ptr(cache_seqlens), batch, s_q, h_q, h_kv, head_dim_v,
+                           _ptr(meta), _ptr(splits), info, _stream()))
+    return Plan(meta, splits, info, ws, (batch, s_q, h_q, h_kv, head_dim_v, bool(kv_fp8)))
 
 
 def _ws(plan):
@@ -112,7 +122,7 @@ def mla_decode(q, kv_cache, block_table, cache_seqlens, softmax_scale, causal=Fa
         raise ValueError("batch mismatch")
     if plan is None:
         plan = mla_decode_plan(cache_seqlens, T, H, 1, MLA_DV)
-    if plan.shape != (B, T, H, 1, MLA_DV):
+    if plan.shape != (B, T, H, 1, MLA_DV, False):
         raise ValueError(f"plan was made for {plan.shape}")
     if out is None:
         out = torch.empty(B, T, H, MLA_DV, dtype=torch.bfloat16, device=q.device)
@@ -174,7 +184,7 @@ def gqa_decode(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, c
         raise ValueError("gqa_decode expects q [..., 128] and k/v caches [P, 64, h_kv, 128]")
     if plan is None:
         plan = mla_decode_plan(cache_seqlens, T, H, G, GQA_D)
-    if plan.shape != (B, T, H, G, GQA_D):
+    if plan.shape != (B, T, H, G, GQA_D, False):
         raise ValueError(f"plan was made for {plan.shape}")
     if out is None:
         out = torch.empty(B, T, H, GQA_D, dtype=torch.bfloat16, device=q.device)
@@ -292,8 +302,8 @@ def mla_decode_fp8(q, kv_codes, kv_scales, block_table, cache_seqlens, softmax_s
     if block_table.shape[0] != B or cache_seqlens.shape[0] != B:
         raise ValueError("batch mismatch")
     if plan is None:
-        plan = mla_decode_plan(cache_seqlens, T, H, 1, MLA_DV)
-    if plan.shape != (B, T, H, 1, MLA_DV):
+        plan = mla_decode_plan(cache_seqlens, T, H, 1, MLA_DV, kv_fp8=True)
+    if plan.shape != (B, T, H, 1, MLA_DV, True):
         raise ValueError(f"plan was made for {plan.shape}")
     if out is None:
         out = torch.empty(B, T, H, MLA_DV, dtype=torch.bfloat16, device=q.device)
@@ -405,7 +415,7 @@ def gqla_decode(q, k_cache, v_cache, block_table, cache_seqlens, softmax_scale, 
                          "v_cache [P, 64, h_kv, 128]")
     if plan is None:
         plan = mla_decode_plan(cache_seqlens, T, H, G, GQLA_DV)
-    if plan.shape != (B, T, H, G, GQLA_DV):
+    if plan.shape != (B, T, H, G, GQLA_DV, False):
         raise ValueError(f"plan was made for {plan.shape}")
     if out is None:
         out = torch.empty(B, T, H, GQLA_DV, dtype=torch.bfloat16, device=q.device)

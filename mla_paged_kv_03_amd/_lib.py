@@ -28,6 +28,7 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _SIGS = {
     "mla_decode_plan": [_P, _I, _I, _I, _I, _I, _P, _P, ctypes.POINTER(PlanInfo), _P],
+    "mla_decode_plan_fp8": [_P, _I, _I, _I, _P, _P, ctypes.POINTER(PlanInfo), _P],
     "mla_decode": [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P,
                    ctypes.c_size_t, _P, _P, _P],
     "mla_decode_noalloc": [_P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P, _P],

@@ -70,7 +70,9 @@ struct Geom {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int make_geom(int B, int T, int H, int G, int DV, int cus, Geom* g) {
+// fp8: the geometry of the FP8 latent decode, whose workgroups hold 64
+// rows at any row count (its plan comes from mla_decode_plan_fp8)
+int make_geom(int B, int T, int H, int G, int DV, int cus, Geom* g, bool fp8 = false) {
   if (B < 0 || T < 1 || H < 1 || G < 1 || H % G != 0) return MLA_ERR_BAD_SHAPE;
   if ((int64_t)T * H > (1 << 20)) return MLA_ERR_UNSUPPORTED;
   memset(g, 0, sizeof(*g));
@@ -90,7 +92,7 @@ int make_geom(int B, int T, int H, int G, int DV, int cus, Geom* g) {
   const int rows = 16 * g->nw;
   g->nrb = (g->M + rows - 1) / rows;
   g->RB = G * g->nrb;
-  g->big = !g->gqa && g->M >= 128;
+  g->big = !g->gqa && g->M >= 128 && !fp8;
   g->nrb128 = (g->M + 127) / 128;
   g->fix = g->big ? sched::FIX_LATENT128 : sched::FIX_DEFAULT;
   // one workgroup per CU for the latent cache (two 72 KiB page buffers);
@@ -146,7 +148,8 @@ int run_decode(int B, int T, int H, int G, int DV, int kind, const void* q, cons
                hipStream_t st) {
   Geom g;
   int rc, cus = 0;
-  if ((rc = make_geom(B, T, H, G, DV, 1, &g)) != MLA_OK) return rc;
+  const bool fp8 = kind == mla::KIND_MLA_FP8;
+  if ((rc = make_geom(B, T, H, G, DV, 1, &g, fp8)) != MLA_OK) return rc;
   if (B == 0) return MLA_OK;  // nothing to read or write (buffers may be empty)
   if ((rc = check_decode_args(g.gqa, q, k, v, block_table, seqlens, num_pages, max_pages, scale,
                               causal, meta, splits, out, lse)) != MLA_OK)
@@ -154,7 +157,7 @@ int run_decode(int B, int T, int H, int G, int DV, int kind, const void* q, cons
   if (kind == mla::KIND_MLA_FP8 && (!kscale || ((uintptr_t)kscale & 3)))
     return kscale ? MLA_ERR_BAD_SHAPE : MLA_ERR_NULL_ARG;
   if ((rc = device_cus(&cus)) != MLA_OK) return rc;
-  make_geom(B, T, H, G, DV, cus, &g);
+  make_geom(B, T, H, G, DV, cus, &g, fp8);
   if (g.ws_bytes) {
     if (!ws) return MLA_ERR_NULL_ARG;
     if (ws_bytes < g.ws_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
@@ -271,24 +274,40 @@ int gqla_heads(int32_t n_tokens, int32_t h_q, int32_t h_kv) {
 
 extern "C" {
 
-int mla_decode_plan(const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
-                    int32_t h_kv, int32_t head_dim_v, int32_t* sched_metadata,
-                    int32_t* num_splits, mla_plan_info* info, hipStream_t stream) {
+namespace {
+int make_plan(const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+              int32_t h_kv, int32_t head_dim_v, bool fp8, int32_t* sched_metadata,
+              int32_t* num_splits, mla_plan_info* info, hipStream_t stream) {
   if (!info) return MLA_ERR_NULL_ARG;
   int cus = 0, rc;
   Geom g;
-  if ((rc = make_geom(batch, s_q, h_q, h_kv, head_dim_v, 1, &g)) != MLA_OK) return rc;
+  if ((rc = make_geom(batch, s_q, h_q, h_kv, head_dim_v, 1, &g, fp8)) != MLA_OK) return rc;
   if ((sched_metadata || num_splits) &&
       (!sched_metadata || !num_splits || (batch > 0 && !cache_seqlens)))
     return MLA_ERR_NULL_ARG;
   if ((rc = device_cus(&cus)) != MLA_OK) return rc;
-  make_geom(batch, s_q, h_q, h_kv, head_dim_v, cus, &g);
+  make_geom(batch, s_q, h_q, h_kv, head_dim_v, cus, &g, fp8);
   fill_info(g, info);
   if (!sched_metadata && !num_splits) return MLA_OK;
   if (mla::launch_plan_kernel(cache_seqlens, batch, g.W, g.TH, g.G, g.DV, g.fix, sched_metadata,
                               num_splits, stream) != hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;
+}
+}  // namespace
+
+int mla_decode_plan(const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                    int32_t h_kv, int32_t head_dim_v, int32_t* sched_metadata,
+                    int32_t* num_splits, mla_plan_info* info, hipStream_t stream) {
+  return make_plan(cache_seqlens, batch, s_q, h_q, h_kv, head_dim_v, false, sched_metadata,
+                   num_splits, info, stream);
+}
+
+int mla_decode_plan_fp8(const int32_t* cache_seqlens, int32_t batch, int32_t s_q, int32_t h_q,
+                        int32_t* sched_metadata, int32_t* num_splits, mla_plan_info* info,
+                        hipStream_t stream) {
+  return make_plan(cache_seqlens, batch, s_q, h_q, 1, MLA_DV, true, sched_metadata, num_splits,
+                   info, stream);
 }
 
 int mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,

@@ -26,7 +26,7 @@ def test_every_declared_function_is_exported(L):
             "gqa_kv_append", "gqla_expand_kv", "gqla_absorb_query", "gqla_absorb_output",
             "gqla_decode", "mla_decode_fp8", "mla_kv_append_fp8",
             "mla_kv_quantize_fp8", "mla_check_pages", "mla_decode_noalloc",
-            "mla_check_fp8_scales"} <= set(names)
+            "mla_check_fp8_scales", "mla_decode_plan_fp8"} <= set(names)
     for name in names:
         assert hasattr(L, name), name
 
@@ -115,6 +115,18 @@ def test_check_pages_argument_checks(L):
     assert L.mla_check_pages(p, p, 2, 0, 4, p, None) == -2
     assert L.mla_check_pages(p, p, 2, 10, 0, p, None) == -2
     assert L.mla_check_pages(p, p, 2, 10, 4, ctypes.c_void_p(66), None) == -2
+
+
+def test_fp8_plan_argument_checks(L):
+    """The FP8 decode's plan checks its arguments as mla_decode_plan does
+    (the sizes need a device: tests/test_plan_guard_gpu.py)."""
+    info = PlanInfo()
+    assert L.mla_decode_plan_fp8(None, 2, 1, 8, None, None, None, None) == -1
+    assert L.mla_decode_plan_fp8(None, -1, 1, 8, None, None, ctypes.byref(info), None) == -2
+    assert L.mla_decode_plan_fp8(None, 2, 0, 8, None, None, ctypes.byref(info), None) == -2
+    p = ctypes.c_void_p(64)
+    assert L.mla_decode_plan_fp8(None, 2, 1, 8, p, p, ctypes.byref(info), None) == -1
+    assert L.mla_decode_plan_fp8(None, 2, 1, 8, p, None, ctypes.byref(info), None) == -1
 
 
 def test_check_fp8_scales_argument_checks(L):

@@ -96,6 +96,7 @@ def test_captured_fp8_and_gqla_steps_replay_like_eager(dev):
     sl = torch.from_numpy(d["cache_seqlens"]).to(dev)
     B, T, H, G = cfg.batch, cfg.s_q, cfg.h_q, cfg.h_kv
     plan_a = lib.mla_decode_plan(sl, T, H, 1, 512)
+    plan_8 = lib.mla_decode_plan(sl, T, H, 1, 512, kv_fp8=True)
     plan_g = lib.mla_decode_plan(sl, T, H, G, 128)
     codes, scales = lib.mla_kv_quantize_fp8(t["kv"])
     qa = torch.empty(B, T, H, 576, dtype=torch.bfloat16, device=dev)
@@ -115,7 +116,7 @@ def test_captured_fp8_and_gqla_steps_replay_like_eager(dev):
         lib.gqla_decode(t["q"], k_rows, v_rows, bt, sl, cfg.scale, cfg.causal, plan=plan_g,
                         out=out_g, lse=lse[1])
         lib.mla_kv_quantize_fp8(t["kv"], codes, scales)
-        lib.mla_decode_fp8(qa, codes, scales, bt, sl, cfg.scale, cfg.causal, plan=plan_a,
+        lib.mla_decode_fp8(qa, codes, scales, bt, sl, cfg.scale, cfg.causal, plan=plan_8,
                            out=o8, lse=lse[2])
 
     s = torch.cuda.Stream()
@@ -151,14 +152,14 @@ def test_captured_fp8_decode_at_64_rows_replays_like_eager(dev):
     import mla_paged_kv_03_amd as lib
     cfg, live = _mla_inputs(dev, 2, "mixed")
     B, T, H = cfg.batch, cfg.s_q, cfg.h_q
-    plan = lib.mla_decode_plan(live["sl"], T, H, 1, 512)
+    plan = lib.mla_decode_plan(live["sl"], T, H, 1, 512, kv_fp8=True)
     codes, scales = lib.mla_kv_quantize_fp8(live["kv"])
     out = torch.empty(B, T, H, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(B, T, H, dtype=torch.float32, device=dev)
 
     def step():
-        lib._lib.check("mla_decode_plan", lib._lib.lib().mla_decode_plan(
-            lib._ptr(live["sl"]), B, T, H, 1, 512, lib._ptr(plan.sched_metadata),
+        lib._lib.check("mla_decode_plan_fp8", lib._lib.lib().mla_decode_plan_fp8(
+            lib._ptr(live["sl"]), B, T, H, lib._ptr(plan.sched_metadata),
             lib._ptr(plan.num_splits), ctypes.byref(plan.info), lib._stream()))
         lib.mla_kv_quantize_fp8(live["kv"], codes, scales)
         lib.mla_decode_fp8(live["q"], codes, scales, live["bt"], live["sl"], cfg.scale,

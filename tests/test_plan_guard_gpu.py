@@ -100,3 +100,54 @@ def test_plan_for_other_kv_heads_leaves_outputs_untouched(dev):
     log("[case] gqa plan for h_kv=4 used for h_kv=8")
     rc, ob, lse = _call(d, t, wrong, 1, 64, 8, max(need, 256))
     assert rc == 0 and _untouched(ob, lse)
+
+
+def test_fp8_decode_takes_its_own_plan_at_128_heads(dev):
+    """From 128 query rows per KV head on, the FP8 decode's plan (64-row
+    workgroups: a worker per CU and row block) differs from the bf16
+    decode's: the bf16 plan leaves the FP8 decode's outputs untouched, the
+    FP8 plan gives the binding's result bit for bit. Below 128 rows the two
+    plans have the same sizes."""
+    import torch
+    import mla_paged_kv_03_amd as lib
+    from mla_paged_kv_03_amd import _lib
+    for s_q, h_q in [(1, 8), (1, 16), (2, 32)]:
+        a, b = lib.plan_info(4, s_q, h_q), lib.plan_info(4, s_q, h_q, kv_fp8=True)
+        assert (a.num_workers, a.metadata_bytes, a.workspace_bytes) == \
+            (b.num_workers, b.metadata_bytes, b.workspace_bytes)
+    a, b = lib.plan_info(4, 1, 128), lib.plan_info(4, 1, 128, kv_fp8=True)
+    assert b.row_blocks == 2 and 2 * b.num_workers == a.num_workers
+    cfg = _mla(4, 1, 128, (5000, 64, 3000, 1), False)
+    d = inputs(cfg, seed=24)
+    t = to_device(d, dev)
+    codes, scales = lib.mla_kv_quantize_fp8(t["kv"])
+    B, T, H = 4, 1, 128
+    P = lambda x: ctypes.c_void_p(x.data_ptr())
+    L = _lib.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def call(plan):
+        need = max(plan.info.workspace_bytes, 256)
+        ws = torch.empty(need // 4 + 64, dtype=torch.float32, device=dev)
+        p = ws.data_ptr()
+        out = torch.full((B, T, H, 512), SENTINEL_OUT, dtype=torch.int16, device=dev)
+        lse = torch.full((B, T, H), SENTINEL_LSE, dtype=torch.float32, device=dev)
+        rc = L.mla_decode_fp8(P(t["q"]), P(codes), P(scales), P(t["block_table"]),
+                              P(t["cache_seqlens"]), B, T, H, codes.shape[0],
+                              t["block_table"].shape[1], cfg.scale, int(cfg.causal),
+                              P(plan.sched_metadata), P(plan.num_splits),
+                              ctypes.c_void_p(p + (-p) % 256), need, P(out), P(lse), stream)
+        torch.cuda.synchronize()
+        return rc, out.cpu().numpy(), lse.cpu().numpy()
+
+    log("[case] fp8 decode at 128 heads with the bf16 plan")
+    rc, ob, lse = call(lib.mla_decode_plan(t["cache_seqlens"], T, H))
+    assert rc == 0 and _untouched(ob, lse)
+    log("[case] fp8 decode at 128 heads with its own plan")
+    rc, ob, lse = call(lib.mla_decode_plan(t["cache_seqlens"], T, H, kv_fp8=True))
+    assert rc == 0
+    ref_o, ref_l = lib.mla_decode_fp8(t["q"], codes, scales, t["block_table"],
+                                      t["cache_seqlens"], cfg.scale, cfg.causal)
+    torch.cuda.synchronize()
+    assert np.array_equal(ob, ref_o.view(torch.int16).cpu().numpy())
+    assert np.array_equal(lse, ref_l.cpu().numpy())
