@@ -100,7 +100,8 @@ typedef struct {
  *
  * sched_metadata opens with 8 int32 words that record the geometry the plan
  * was made for: a fixed tag 0x4D4C4150, the worker count, batch, s_q * h_q,
- * h_kv and head_dim_v (then two zero words). The decode kernels and their
+ * h_kv and head_dim_v, then the plan's overhead units per piece of a
+ * sequence and the batch's total cost in units. The decode kernels and their
  * internal merge compare this signature with their own call before they
  * read any worker record or slot; on a mismatch (a plan made for another
  * batch, s_q * h_q, h_kv, value width or device) they return at once and

@@ -61,7 +61,7 @@ struct Geom {
   // blocks (nrb of them per worker) over the same workers
   bool big;
   int nrb128;
-  int fix;    // per-sequence overhead units of the plan (schedule.h)
+  int fix;    // overhead units per piece of a sequence in the plan (schedule.h)
   int W;      // workers
   int TH;
   int max_slots;

@@ -339,8 +339,8 @@ def test_workspace_size_matches_slot_bound():
 def test_plan_opens_with_its_geometry(shape):
     """The metadata starts with a signature: a fixed tag, the worker count,
     the batch, the rows per sequence (s_q * h_q), the KV heads, the value
-    width and the plan's per-sequence overhead units; the decode and merge
-    kernels compare the first six with their own call."""
+    width, the plan's overhead units per piece and the batch's total cost;
+    the decode and merge kernels compare the first six with their own call."""
     T, H, G, dv = shape
     seqlens = [100, 0, 5000]
     meta, splits, info = mla_decode_plan_host(seqlens, T, H, G, dv, num_cus=256)
