@@ -84,29 +84,42 @@ __device__ __forceinline__ void scores_ready(f32x16& s0, f32x16& s1) {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Scalar loads from wave-uniform addresses, issued together and waited for
-// in the same statement: one memory round trip for all of them. The block
+// in the same statement: one memory round trip for all of them. Each block
 // opens with one wait state after a possible VALU write of the address
 // registers; the results are early-clobber, so no result register doubles as
 // an address still to be read.
-__device__ __forceinline__ void sload6(const int32_t* p, int (&v)[6]) {
-  int a0, a1, a2, a3, a4, a5;
+
+// The first six words at p and at q in one round trip (the plan's signature
+// and this worker's record, which do not depend on each other).
+__device__ __forceinline__ void sload6x2(const int32_t* p, const int32_t* q, int (&u)[6],
+                                         int (&v)[6]) {
+  int a0, a1, a2, a3, a4, a5, b0, b1, b2, b3, b4, b5;
   asm volatile(
-      "s_nop 0\n\ts_load_dword %0, %6, 0x0\n\ts_load_dword %1, %6, 0x4\n\t"
-      "s_load_dword %2, %6, 0x8\n\ts_load_dword %3, %6, 0xc\n\ts_load_dword %4, %6, 0x10\n\t"
-      "s_load_dword %5, %6, 0x14\n\ts_waitcnt lgkmcnt(0)"
-      : "=&s"(a0), "=&s"(a1), "=&s"(a2), "=&s"(a3), "=&s"(a4), "=&s"(a5)
-      : "s"(p)
-      : "memory");
-  v[0] = a0; v[1] = a1; v[2] = a2; v[3] = a3; v[4] = a4; v[5] = a5;
-}
-// *p, *q and *(q + 1) in one round trip
-__device__ __forceinline__ void sload_1_2(const int32_t* p, const int32_t* q, int& x, int& y0,
-                                          int& y1) {
-  asm volatile(
-      "s_nop 0\n\ts_load_dword %0, %3, 0x0\n\ts_load_dword %1, %4, 0x0\n\t"
-      "s_load_dword %2, %4, 0x4\n\ts_waitcnt lgkmcnt(0)"
-      : "=&s"(x), "=&s"(y0), "=&s"(y1)
+      "s_nop 0\n\ts_load_dword %0, %12, 0x0\n\ts_load_dword %1, %12, 0x4\n\t"
+      "s_load_dword %2, %12, 0x8\n\ts_load_dword %3, %12, 0xc\n\ts_load_dword %4, %12, 0x10\n\t"
+      "s_load_dword %5, %12, 0x14\n\t"
+      "s_load_dword %6, %13, 0x0\n\ts_load_dword %7, %13, 0x4\n\t"
+      "s_load_dword %8, %13, 0x8\n\ts_load_dword %9, %13, 0xc\n\ts_load_dword %10, %13, 0x10\n\t"
+      "s_load_dword %11, %13, 0x14\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(a0), "=&s"(a1), "=&s"(a2), "=&s"(a3), "=&s"(a4), "=&s"(a5), "=&s"(b0), "=&s"(b1),
+        "=&s"(b2), "=&s"(b3), "=&s"(b4), "=&s"(b5)
       : "s"(p), "s"(q)
+      : "memory");
+  u[0] = a0; u[1] = a1; u[2] = a2; u[3] = a3; u[4] = a4; u[5] = a5;
+  v[0] = b0; v[1] = b1; v[2] = b2; v[3] = b3; v[4] = b4; v[5] = b5;
+}
+// A sequence's length *p, its slot range *q and *(q + 1), and the
+// block-table entries *r0 and *r1 (its first two pages in this range), in
+// one round trip.
+__device__ __forceinline__ void sload_seq(const int32_t* p, const int32_t* q, const int32_t* r0,
+                                          const int32_t* r1, int& x, int& y0, int& y1, int& z0,
+                                          int& z1) {
+  asm volatile(
+      "s_nop 0\n\ts_load_dword %0, %5, 0x0\n\ts_load_dword %1, %6, 0x0\n\t"
+      "s_load_dword %2, %6, 0x4\n\ts_load_dword %3, %7, 0x0\n\ts_load_dword %4, %8, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(x), "=&s"(y0), "=&s"(y1), "=&s"(z0), "=&s"(z1)
+      : "s"(p), "s"(q), "s"(r0), "s"(r1)
       : "memory");
 }
 
@@ -154,19 +167,22 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
   int w, rb;
   decode_block_id(blockIdx.x, a.W, a.nrb, w, rb);
 
-  // a plan made for another geometry: leave every output untouched
-  const int32_t* hdr = a.meta;
-  if (hdr[sched::H_MAGIC] != sched::PLAN_MAGIC || hdr[sched::H_W] != a.W ||
-      hdr[sched::H_B] != a.B || hdr[sched::H_ROWS] != a.T * a.H || hdr[sched::H_G] != a.G ||
-      hdr[sched::H_DV] != LY::DV)
-    return;
-  // wave-uniform values come in by scalar loads
+  // wave-uniform values come in by scalar loads: the plan's signature and
+  // this worker's record together (the record is used only once the
+  // signature matches)
   const int32_t* rec = uniform_ptr(sched::records(a.meta) + w * sched::REC);
   static_assert(sched::R_B_START < 6 && sched::R_B_END < 6 && sched::R_OWNS_FIRST < 6 &&
                     sched::R_SPLIT0 < 6 && sched::R_P_START < 6 && sched::R_P_END < 6,
                 "the record words read here are its first six");
-  int rw[6];
-  sload6(rec, rw);
+  static_assert(sched::H_MAGIC < 6 && sched::H_W < 6 && sched::H_B < 6 && sched::H_ROWS < 6 &&
+                    sched::H_G < 6 && sched::H_DV < 6,
+                "the signature words compared here are its first six");
+  int hw[6], rw[6];
+  sload6x2(uniform_ptr(a.meta), rec, hw, rw);
+  // a plan made for another geometry: leave every output untouched
+  if (hw[sched::H_MAGIC] != sched::PLAN_MAGIC || hw[sched::H_W] != a.W || hw[sched::H_B] != a.B ||
+      hw[sched::H_ROWS] != a.T * a.H || hw[sched::H_G] != a.G || hw[sched::H_DV] != LY::DV)
+    return;
   const int bs = rw[sched::R_B_START];
   const int be = rw[sched::R_B_END];
   if (be < bs) return;
@@ -232,8 +248,18 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
   const int32_t* seqlens = uniform_ptr(a.seqlens);
   const int32_t* slots = uniform_ptr(a.slots);
   for (int b = bs; b <= be; ++b) {
-    int L, s0, s1;
-    sload_1_2(seqlens + b, slots + b, L, s0, s1);
+    const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+    // the entries of the range's first two pages are looked up with the
+    // length: the record fixes where the range starts. The indices are
+    // clamped into the row, so the lookups stay inside the block table
+    // whatever the lengths (they differ from p0 and p0 + 1 only where a
+    // length needs more pages than a row holds); an entry past the
+    // sequence's pages is loaded but not used.
+    const int pa = min(max(b == bs ? p_start : 0, 0), a.bt_stride - 1);
+    const int pb = min(pa + 1, a.bt_stride - 1);
+    int L, s0, s1, pg_a, pg_b;
+    sload_seq(seqlens + b, slots + b, uniform_ptr(bt + pa), uniform_ptr(bt + pb), L, s0, s1, pg_a,
+              pg_b);
     const int npg = sched::seq_pages(L);
     // the page range of schedule.h's page_range, from the record's words
     int p0 = b == bs ? p_start : 0;
@@ -256,7 +282,6 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
     }
     if (p0 >= p1) continue;
     const int split = b == bs ? split0 : 0;
-    const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
 
     // queries of this lane's row: B operand of the score MFMA, columns
     // 16c + 8hf .. +7 at step c; loaded once the first page's copies are in
@@ -289,12 +314,14 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
     // rows at or past it return zeros, finite values whose keys the mask
     // drops. With valid == false they cover nothing: the copies then move
     // no data, and every wave still issues the same copies on every page.
-    auto page_rsrc = [&](int j, bool valid, i32x4& lo, i32x4& hi) {
-      const int page = sload(uniform_ptr(bt + j));
+    auto page_rsrc_of = [&](int j, int page, bool valid, i32x4& lo, i32x4& hi) {
       const char* base = (const char*)a.k + (size_t)page * LY::TILE;
       const int nb = valid ? min(64, L - 64 * j) * 1152 : 0;
       lo = buffer_rsrc(base, (uint32_t)nb);
       hi = buffer_rsrc(base + 8 * 1152, (uint32_t)max(nb - 8 * 1152, 0));
+    };
+    auto page_rsrc = [&](int j, bool valid, i32x4& lo, i32x4& hi) {
+      page_rsrc_of(j, sload(uniform_ptr(bt + j)), valid, lo, hi);
     };
     // copy T (a literal, 0 .. 17) of this wave into the page buffer at LDS
     // byte BUF0
@@ -328,7 +355,7 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
 
       {  // page p0 into buffer 0
         i32x4 lo, hi;
-        page_rsrc(p0, true, lo, hi);
+        page_rsrc_of(p0, pg_a, true, lo, hi);
         MLA_DMA_ALL(lo, hi, lds0);
       }
       if constexpr (MODE == PASS_FIRST_REF) load_q();
@@ -336,7 +363,10 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
         const int cur = (j - p0) & 1;
         const bool has_next = j + 1 < p1;
         i32x4 nlo, nhi;
-        page_rsrc(has_next ? j + 1 : j, has_next, nlo, nhi);
+        if (j == p0 && has_next)
+          page_rsrc_of(j + 1, pg_b, true, nlo, nhi);
+        else
+          page_rsrc(has_next ? j + 1 : j, has_next, nlo, nhi);
         const uint32_t ndst = lds0 + (cur ^ 1) * LY::TILE;
         // this wave's copies of page j have landed; after the barrier every
         // wave's have, and every wave is done with page j - 1, whose buffer
