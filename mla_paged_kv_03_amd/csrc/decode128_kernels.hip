@@ -123,6 +123,14 @@ __device__ __forceinline__ void sload_seq(const int32_t* p, const int32_t* q, co
       : "memory");
 }
 
+// *p and *q in one round trip
+__device__ __forceinline__ void sload_2(const int32_t* p, const int32_t* q, int& x, int& y) {
+  asm volatile("s_nop 0\n\ts_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(x), "=&s"(y)
+               : "s"(p), "s"(q)
+               : "memory");
+}
+
 // Raw buffer descriptor of n bytes from p (no stride, 32-bit data format):
 // loads at offsets >= n return zeros and read no memory.
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* p, uint32_t n) {
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
   const int hf = lane >> 5;  // which half of each MFMA's 16 k-slots the lane holds
 
   int w, rb;
-  decode_block_id(blockIdx.x, a.W, a.nrb, w, rb);
+  decode_block_id_xcd(blockIdx.x, a.W, a.nrb, w, rb);
 
   // wave-uniform values come in by scalar loads: the plan's signature and
   // this worker's record together (the record is used only once the
@@ -247,19 +255,51 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
 
   const int32_t* seqlens = uniform_ptr(a.seqlens);
   const int32_t* slots = uniform_ptr(a.slots);
-  for (int b = bs; b <= be; ++b) {
+  // The length, slot range and first two block-table entries of sequence b
+  // (pages from p0 on) in one round trip. The indices are clamped into the
+  // row, so the lookups stay inside the block table whatever the lengths
+  // (they differ from p0 and p0 + 1 only where a length needs more pages
+  // than a row holds); an entry past the sequence's pages is loaded but not
+  // used.
+  auto lookup = [&](int b, int p0, int& L, int& s0, int& s1, int& pg_a, int& pg_b) {
     const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
-    // the entries of the range's first two pages are looked up with the
-    // length: the record fixes where the range starts. The indices are
-    // clamped into the row, so the lookups stay inside the block table
-    // whatever the lengths (they differ from p0 and p0 + 1 only where a
-    // length needs more pages than a row holds); an entry past the
-    // sequence's pages is loaded but not used.
-    const int pa = min(max(b == bs ? p_start : 0, 0), a.bt_stride - 1);
+    const int pa = min(max(p0, 0), a.bt_stride - 1);
     const int pb = min(pa + 1, a.bt_stride - 1);
-    int L, s0, s1, pg_a, pg_b;
     sload_seq(seqlens + b, slots + b, uniform_ptr(bt + pa), uniform_ptr(bt + pb), L, s0, s1, pg_a,
               pg_b);
+  };
+  // Descriptors of a page's two halves of rows (rows 0..7 and 8..15 of each
+  // wave's 16) holding its first nb bytes: copies past them return zeros
+  // (finite values whose keys the mask drops) and read nothing, so every
+  // wave issues the same copies on every page.
+  auto make_rsrc = [&](int page, int nb, i32x4& lo, i32x4& hi) {
+    const char* base = (const char*)a.k + (size_t)page * LY::TILE;
+    lo = buffer_rsrc(base, (uint32_t)nb);
+    hi = buffer_rsrc(base + 8 * 1152, (uint32_t)max(nb - 8 * 1152, 0));
+  };
+  // copy T (a literal, 0 .. 17) of this wave into the page buffer at LDS
+  // byte BUF0
+#define MLA_DMA_ONE(T, LO, HI, BUF0)                                              \
+  dma16_buf<1024 * (T)>((BUF0) + wave * (16 * 1152), (T) < 9 ? (LO) : (HI),       \
+                        (T) < 9 ? dma_off[(T) < 9 ? (T) : 0] : dma_off[(T) < 9 ? 0 : (T) - 9] ^ 16u)
+#define MLA_DMA_ALL(LO, HI, BUF0)                                                                 \
+  MLA_DMA_ONE(0, LO, HI, BUF0); MLA_DMA_ONE(1, LO, HI, BUF0); MLA_DMA_ONE(2, LO, HI, BUF0);     \
+  MLA_DMA_ONE(3, LO, HI, BUF0); MLA_DMA_ONE(4, LO, HI, BUF0); MLA_DMA_ONE(5, LO, HI, BUF0);     \
+  MLA_DMA_ONE(6, LO, HI, BUF0); MLA_DMA_ONE(7, LO, HI, BUF0); MLA_DMA_ONE(8, LO, HI, BUF0);     \
+  MLA_DMA_ONE(9, LO, HI, BUF0); MLA_DMA_ONE(10, LO, HI, BUF0); MLA_DMA_ONE(11, LO, HI, BUF0);   \
+  MLA_DMA_ONE(12, LO, HI, BUF0); MLA_DMA_ONE(13, LO, HI, BUF0); MLA_DMA_ONE(14, LO, HI, BUF0);  \
+  MLA_DMA_ONE(15, LO, HI, BUF0); MLA_DMA_ONE(16, LO, HI, BUF0); MLA_DMA_ONE(17, LO, HI, BUF0)
+
+  // whether the current sequence's first page went into buffer 0 before
+  // the epilogue of the sequence ahead of it
+  bool next_page = false;
+
+  for (int b = bs; b <= be; ++b) {
+    const int32_t* bt = a.block_table + (size_t)b * a.bt_stride;
+    int L, s0, s1, pg_a, pg_b;
+    lookup(b, b == bs ? p_start : 0, L, s0, s1, pg_a, pg_b);
+    const bool page_issued = next_page;
+    next_page = false;
     const int npg = sched::seq_pages(L);
     // the page range of schedule.h's page_range, from the record's words
     int p0 = b == bs ? p_start : 0;
@@ -309,32 +349,14 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
     // keys below this are visible to every row of the workgroup
     const int vis_all = a.causal ? L - a.T + 1 : L;
 
-    // Descriptors of page j's two halves of rows (rows 0..7 and 8..15 of
-    // each wave's 16), covering the rows below the sequence end: copies of
-    // rows at or past it return zeros, finite values whose keys the mask
-    // drops. With valid == false they cover nothing: the copies then move
-    // no data, and every wave still issues the same copies on every page.
+    // page j of this sequence: valid == false covers nothing (the copies
+    // then move no data)
     auto page_rsrc_of = [&](int j, int page, bool valid, i32x4& lo, i32x4& hi) {
-      const char* base = (const char*)a.k + (size_t)page * LY::TILE;
-      const int nb = valid ? min(64, L - 64 * j) * 1152 : 0;
-      lo = buffer_rsrc(base, (uint32_t)nb);
-      hi = buffer_rsrc(base + 8 * 1152, (uint32_t)max(nb - 8 * 1152, 0));
+      make_rsrc(page, valid ? min(64, L - 64 * j) * 1152 : 0, lo, hi);
     };
     auto page_rsrc = [&](int j, bool valid, i32x4& lo, i32x4& hi) {
       page_rsrc_of(j, sload(uniform_ptr(bt + j)), valid, lo, hi);
     };
-    // copy T (a literal, 0 .. 17) of this wave into the page buffer at LDS
-    // byte BUF0
-#define MLA_DMA_ONE(T, LO, HI, BUF0)                                              \
-  dma16_buf<1024 * (T)>((BUF0) + wave * (16 * 1152), (T) < 9 ? (LO) : (HI),       \
-                        (T) < 9 ? dma_off[(T) < 9 ? (T) : 0] : dma_off[(T) < 9 ? 0 : (T) - 9] ^ 16u)
-#define MLA_DMA_ALL(LO, HI, BUF0)                                                                 \
-  MLA_DMA_ONE(0, LO, HI, BUF0); MLA_DMA_ONE(1, LO, HI, BUF0); MLA_DMA_ONE(2, LO, HI, BUF0);     \
-  MLA_DMA_ONE(3, LO, HI, BUF0); MLA_DMA_ONE(4, LO, HI, BUF0); MLA_DMA_ONE(5, LO, HI, BUF0);     \
-  MLA_DMA_ONE(6, LO, HI, BUF0); MLA_DMA_ONE(7, LO, HI, BUF0); MLA_DMA_ONE(8, LO, HI, BUF0);     \
-  MLA_DMA_ONE(9, LO, HI, BUF0); MLA_DMA_ONE(10, LO, HI, BUF0); MLA_DMA_ONE(11, LO, HI, BUF0);   \
-  MLA_DMA_ONE(12, LO, HI, BUF0); MLA_DMA_ONE(13, LO, HI, BUF0); MLA_DMA_ONE(14, LO, HI, BUF0);  \
-  MLA_DMA_ONE(15, LO, HI, BUF0); MLA_DMA_ONE(16, LO, HI, BUF0); MLA_DMA_ONE(17, LO, HI, BUF0)
 
     f32x16 o[R128_NT];
     float m = -INFINITY, l = 0.f, lw = 0.f;
@@ -353,12 +375,12 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
       if constexpr (MODE != PASS_PRESET_REF) m = -INFINITY;
       bool over = false;
 
-      {  // page p0 into buffer 0
+      if constexpr (MODE != PASS_FIRST_REF) {  // page p0 into buffer 0 (the first
+                                              // pass finds it issued)
         i32x4 lo, hi;
         page_rsrc_of(p0, pg_a, true, lo, hi);
         MLA_DMA_ALL(lo, hi, lds0);
       }
-      if constexpr (MODE == PASS_FIRST_REF) load_q();
       for (int j = p0; j < p1; ++j) {
         const int cur = (j - p0) & 1;
         const bool has_next = j + 1 < p1;
@@ -551,10 +573,36 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
       return over;
     };
 
+    // page p0 into buffer 0, unless it went there before the epilogue of
+    // the sequence ahead; then the queries
+    if (!page_issued) {
+      i32x4 lo, hi;
+      page_rsrc_of(p0, pg_a, true, lo, hi);
+      MLA_DMA_ALL(lo, hi, lds0);
+    }
+    load_q();
     // every wave runs the same passes: the page buffers and barriers are shared
     if (block_or<R128_WAVES>(run_pass(pass_tag<PASS_FIRST_REF>{}), lds_p, wave)) {
       run_pass(pass_tag<PASS_MAX_ONLY>{});
       run_pass(pass_tag<PASS_PRESET_REF>{});
+    }
+
+    // Every wave is past the last page and the flag words: both page
+    // buffers are free. The next sequence's first page goes into buffer 0
+    // now, so that its latency overlaps this sequence's epilogue, which
+    // stages its rows in buffer 1.
+    if (b < be) {
+      int nL, npg_a;  // the next sequence's length and first page
+      sload_2(seqlens + b + 1, uniform_ptr(a.block_table + (size_t)(b + 1) * a.bt_stride), nL,
+              npg_a);
+      const int nnpg = sched::seq_pages(nL);
+      const int np1 = min(b + 1 == be ? p_end : nnpg, nnpg);
+      if (np1 > 0) {  // pages 0 .. np1 - 1 of the next sequence are this worker's
+        i32x4 lo, hi;
+        make_rsrc(npg_a, min(64, nL) * 1152, lo, hi);
+        MLA_DMA_ALL(lo, hi, lds0);
+        next_page = true;
+      }
     }
 
     // ---- epilogue. Lane l holds output columns 32tt + 8q + 4hf .. +3 of
@@ -581,8 +629,8 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
       const bool to_part = nslots != 0;
       const size_t slot = (size_t)(s0 + split);
       constexpr int PITCH = 528;  // staged row: 128 fp32 + 16 bytes of bank skew
-      static_assert(R128_WAVES * 32 * PITCH <= 2 * LY::TILE, "staging fits the page buffers");
-      lds_char* const stage = lds_p + wave * (32 * PITCH);
+      static_assert(R128_WAVES * 32 * PITCH <= LY::TILE, "staging fits one page buffer");
+      lds_char* const stage = lds_p + LY::TILE + wave * (32 * PITCH);
       const int row0 = rb * 128 + wave * 32;  // the wave's first row
       // the row bases stay global pointers: generic ones would make the
       // stores FLAT, which also count against the LDS counter, so every
@@ -671,9 +719,9 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
           a.lse[(size_t)b * TH + rho] = lse_v;
       }
     }
-    // every wave has read its staged rows before the next sequence's first
-    // page lands in the same bytes
-    barrier();
+    // No barrier here: the staging buffer (buffer 1) takes page copies again
+    // only after the next sequence's first barrier, which every wave reaches
+    // once its staged rows are stored; the next first page lands in buffer 0.
   }
 }
 

@@ -25,6 +25,22 @@ __device__ __forceinline__ void decode_block_id(int bid, int W, int RB, int& w, 
   }
 }
 
+// Map a workgroup id to (worker, row block) with each XCD holding a
+// contiguous run of W / 8 workers, all row blocks of each: besides the row
+// blocks of a worker, the neighbouring workers that share the pieces of one
+// split sequence (and so its queries) then share an XCD's L2.
+__device__ __forceinline__ void decode_block_id_xcd(int bid, int W, int RB, int& w, int& rb) {
+  if ((W & 7) == 0) {
+    const int x = bid & 7, k = bid >> 3;
+    const int kw = k / RB;
+    rb = k - kw * RB;
+    w = x * (W >> 3) + kw;
+  } else {
+    w = bid / RB;
+    rb = bid - w * RB;
+  }
+}
+
 // Waves per decode workgroup: four compute waves, plus four copy waves for
 // the latent cache at 64 query rows per workgroup (bf16, or FP8 pages that
 // the copy waves dequantise to bf16), where every page is copied once per
