@@ -666,15 +666,21 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
             }
             __builtin_amdgcn_sched_barrier(0);
           }
-          // a wave's LDS accesses run in issue order: the reads see the writes
+          // a wave's LDS accesses run in issue order: the reads see the
+          // writes. All sixteen reads go out before the first store, so
+          // their latencies overlap (the query registers are free here);
+          // read one at a time, each store waited for its own round trip.
+          f32x4 v[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            v[i] = *(const __attribute__((address_space(3))) f32x4*)(stage + rd + 2 * i * PITCH);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const f32x4 v =
-                *(const __attribute__((address_space(3))) f32x4*)(stage + rd + 2 * i * PITCH);
             if constexpr (PART) {
-              *(__attribute__((address_space(1))) f32x4*)(part_base + el + 2 * i * LY::DV) = v;
+              *(__attribute__((address_space(1))) f32x4*)(part_base + el + 2 * i * LY::DV) = v[i];
             } else {
-              const u32x2 z = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+              const u32x2 z = {pack_bf16x2(v[i][0], v[i][1]), pack_bf16x2(v[i][2], v[i][3])};
               *(__attribute__((address_space(1))) u32x2*)(out_base + el + 2 * i * LY::DV) = z;
             }
           }
