@@ -154,15 +154,24 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void combine_kernel(CombineArgs 
   const int rho = blockIdx.x * COMBINE_ROWS + (threadIdx.x >> 6);
   const int b = blockIdx.y;
   if (rho >= a.R) return;
-  // inside a decode call: the slot prefix must come from a plan made for
-  // this call's geometry, the one the decode kernel checked (else the
-  // slots may lie past the workspace, or hold no partials of this call)
-  if (a.meta && (a.meta[sched::H_MAGIC] != sched::PLAN_MAGIC || a.meta[sched::H_W] != a.W ||
-                 a.meta[sched::H_B] != a.B || a.meta[sched::H_ROWS] != a.R ||
-                 a.meta[sched::H_G] != a.G || a.meta[sched::H_DV] != a.DV))
-    return;
+  // The sequence's slot range (b < B: inside the B + 1 entries whatever
+  // the plan) and, inside a decode call, the plan's signature, all loaded
+  // before any of them is tested so that they share one memory round trip.
+  // The slot prefix must come from a plan made for this call's geometry,
+  // the one the decode kernel checked (else the slots may lie past the
+  // workspace, or hold no partials of this call).
   const int s0 = a.slots[b];
-  const int ns = a.slots[b + 1] - s0;
+  const int s1 = a.slots[b + 1];
+  if (a.meta) {
+    const int32_t* h = a.meta;
+    const int32_t h_magic = h[sched::H_MAGIC], h_w = h[sched::H_W], h_b = h[sched::H_B],
+                  h_rows = h[sched::H_ROWS], h_g = h[sched::H_G], h_dv = h[sched::H_DV];
+    // bitwise, not short-circuit: no load waits for another's comparison
+    if ((h_magic != sched::PLAN_MAGIC) | (h_w != a.W) | (h_b != a.B) | (h_rows != a.R) |
+        (h_g != a.G) | (h_dv != a.DV))
+      return;
+  }
+  const int ns = s1 - s0;
   if (ns <= 0) return;
   // this wave's items: slots s0 + first + i * stride, i < n
   int first = 0, stride = 1, n = ns;

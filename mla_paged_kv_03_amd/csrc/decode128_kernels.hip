@@ -89,24 +89,17 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // registers; the results are early-clobber, so no result register doubles as
 // an address still to be read.
 
-// The first six words at p and at q in one round trip (the plan's signature
-// and this worker's record, which do not depend on each other).
-__device__ __forceinline__ void sload6x2(const int32_t* p, const int32_t* q, int (&u)[6],
-                                         int (&v)[6]) {
-  int a0, a1, a2, a3, a4, a5, b0, b1, b2, b3, b4, b5;
+// The first six words at p in one round trip.
+__device__ __forceinline__ void sload6(const int32_t* p, int (&v)[6]) {
+  int a0, a1, a2, a3, a4, a5;
   asm volatile(
-      "s_nop 0\n\ts_load_dword %0, %12, 0x0\n\ts_load_dword %1, %12, 0x4\n\t"
-      "s_load_dword %2, %12, 0x8\n\ts_load_dword %3, %12, 0xc\n\ts_load_dword %4, %12, 0x10\n\t"
-      "s_load_dword %5, %12, 0x14\n\t"
-      "s_load_dword %6, %13, 0x0\n\ts_load_dword %7, %13, 0x4\n\t"
-      "s_load_dword %8, %13, 0x8\n\ts_load_dword %9, %13, 0xc\n\ts_load_dword %10, %13, 0x10\n\t"
-      "s_load_dword %11, %13, 0x14\n\ts_waitcnt lgkmcnt(0)"
-      : "=&s"(a0), "=&s"(a1), "=&s"(a2), "=&s"(a3), "=&s"(a4), "=&s"(a5), "=&s"(b0), "=&s"(b1),
-        "=&s"(b2), "=&s"(b3), "=&s"(b4), "=&s"(b5)
-      : "s"(p), "s"(q)
+      "s_nop 0\n\ts_load_dword %0, %6, 0x0\n\ts_load_dword %1, %6, 0x4\n\t"
+      "s_load_dword %2, %6, 0x8\n\ts_load_dword %3, %6, 0xc\n\ts_load_dword %4, %6, 0x10\n\t"
+      "s_load_dword %5, %6, 0x14\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(a0), "=&s"(a1), "=&s"(a2), "=&s"(a3), "=&s"(a4), "=&s"(a5)
+      : "s"(p)
       : "memory");
-  u[0] = a0; u[1] = a1; u[2] = a2; u[3] = a3; u[4] = a4; u[5] = a5;
-  v[0] = b0; v[1] = b1; v[2] = b2; v[3] = b3; v[4] = b4; v[5] = b5;
+  v[0] = a0; v[1] = a1; v[2] = a2; v[3] = a3; v[4] = a4; v[5] = a5;
 }
 // A sequence's length *p, its slot range *q and *(q + 1), and the
 // block-table entries *r0 and *r1 (its first two pages in this range), in
@@ -175,22 +168,25 @@ __global__ __launch_bounds__(64 * R128_WAVES) void decode128_kernel(DecodeArgs a
   int w, rb;
   decode_block_id_xcd(blockIdx.x, a.W, a.nrb, w, rb);
 
-  // wave-uniform values come in by scalar loads: the plan's signature and
-  // this worker's record together (the record is used only once the
-  // signature matches)
+  // Wave-uniform values come in by scalar loads. First the plan's signature
+  // (its six words in one round trip): a plan made for another geometry
+  // leaves every output untouched, and its buffer may not even hold this
+  // worker's record, which is read only after the signature matches.
+  static_assert(sched::H_MAGIC < 6 && sched::H_W < 6 && sched::H_B < 6 && sched::H_ROWS < 6 &&
+                    sched::H_G < 6 && sched::H_DV < 6,
+                "the signature words compared here are its first six");
+  int hw[6];
+  sload6(uniform_ptr(a.meta), hw);
+  if ((hw[sched::H_MAGIC] != sched::PLAN_MAGIC) | (hw[sched::H_W] != a.W) |
+      (hw[sched::H_B] != a.B) | (hw[sched::H_ROWS] != a.T * a.H) | (hw[sched::H_G] != a.G) |
+      (hw[sched::H_DV] != LY::DV))
+    return;
   const int32_t* rec = uniform_ptr(sched::records(a.meta) + w * sched::REC);
   static_assert(sched::R_B_START < 6 && sched::R_B_END < 6 && sched::R_OWNS_FIRST < 6 &&
                     sched::R_SPLIT0 < 6 && sched::R_P_START < 6 && sched::R_P_END < 6,
                 "the record words read here are its first six");
-  static_assert(sched::H_MAGIC < 6 && sched::H_W < 6 && sched::H_B < 6 && sched::H_ROWS < 6 &&
-                    sched::H_G < 6 && sched::H_DV < 6,
-                "the signature words compared here are its first six");
-  int hw[6], rw[6];
-  sload6x2(uniform_ptr(a.meta), rec, hw, rw);
-  // a plan made for another geometry: leave every output untouched
-  if (hw[sched::H_MAGIC] != sched::PLAN_MAGIC || hw[sched::H_W] != a.W || hw[sched::H_B] != a.B ||
-      hw[sched::H_ROWS] != a.T * a.H || hw[sched::H_G] != a.G || hw[sched::H_DV] != LY::DV)
-    return;
+  int rw[6];
+  sload6(rec, rw);
   const int bs = rw[sched::R_B_START];
   const int be = rw[sched::R_B_END];
   if (be < bs) return;

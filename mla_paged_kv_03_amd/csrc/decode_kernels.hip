@@ -100,10 +100,12 @@ __global__ __launch_bounds__(64 * decode_waves(R, KIND)) void decode_kernel(Deco
 
   // a plan made for another geometry: leave every output untouched rather
   // than index records or slots that belong to a different layout
+  // (bitwise, not short-circuit: the six words load in one round trip)
   const int32_t* hdr = a.meta;
-  if (hdr[sched::H_MAGIC] != sched::PLAN_MAGIC || hdr[sched::H_W] != a.W ||
-      hdr[sched::H_B] != a.B || hdr[sched::H_ROWS] != a.T * a.H || hdr[sched::H_G] != a.G ||
-      hdr[sched::H_DV] != LY::DV)
+  const int32_t h_magic = hdr[sched::H_MAGIC], h_w = hdr[sched::H_W], h_b = hdr[sched::H_B],
+                h_rows = hdr[sched::H_ROWS], h_g = hdr[sched::H_G], h_dv = hdr[sched::H_DV];
+  if ((h_magic != sched::PLAN_MAGIC) | (h_w != a.W) | (h_b != a.B) | (h_rows != a.T * a.H) |
+      (h_g != a.G) | (h_dv != LY::DV))
     return;
   const int32_t* rec = sched::records(a.meta) + w * sched::REC;
   const int bs = uniform(rec[sched::R_B_START]);
