@@ -305,7 +305,7 @@ def _climbing_scores(d, cfg, period=5, step=18.0, seed=7):
 
 
 @pytest.mark.parametrize("period", [3, 5])
-@pytest.mark.parametrize("kind", ["mla", "mla_h128", "gqa"])
+@pytest.mark.parametrize("kind", ["mla", "mla_h128", "mla_h128_short", "gqa"])
 def test_scores_climbing_from_page_to_page(dev, kind, period):
     """Scores rise by 18 (log2 units) from page to page within runs of
     `period` pages, far more than the rescale slack. With period 3 a row's
@@ -316,9 +316,16 @@ def test_scores_climbing_from_page_to_page(dev, kind, period):
     consecutive pages (the batch has far more pages than workers)."""
     import mla_paged_kv_03_amd as lib
     Ls = (64 * 300, 64 * 280 + 17, 64 * 300, 64 * 290)
-    # 128 heads: the 64-row workgroups whose page copies come from copy waves
+    # 300 sequences of 3 to 8 pages at 128 heads: most workers take one or
+    # two whole sequences, a sequence of five or more pages climbs past the
+    # fixed reference and falls back to the second pass, and the worker then
+    # goes on to its next sequence, whose first page went out before the
+    # epilogue
+    short = tuple(64 * (5, 6, 7, 3, 8)[i % 5] - 7 * (i % 3) for i in range(300))
+    # 128 heads: the 128-row latent kernel
     cfg = {"mla": lambda: _mla(4, 1, 16, Ls, False),
            "mla_h128": lambda: _mla(4, 1, 128, Ls, False),
+           "mla_h128_short": lambda: _mla(300, 1, 128, short, False),
            "gqa": lambda: _gqa(4, 1, 16, 2, Ls)}[kind]()
     d = inputs(cfg, seed=12)
     _climbing_scores(d, cfg, period=period)
