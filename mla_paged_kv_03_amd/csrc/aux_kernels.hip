@@ -44,6 +44,9 @@ __device__ int block_scan(int v, int* wsum, int* total) {
 // LDS, where the workers' binary searches run; larger ones search them in
 // global memory.
 constexpr int PLAN_LDS_SEQS = 8192;
+// Plans over up to this many workers find each worker's first and last
+// sequences through an LDS table filled by the sequences (below).
+constexpr int PLAN_LDS_WORKERS = 2048;
 
 // One workgroup. Writes the plan's signature, the unit prefix (B + 1 entries
 // after the W worker records), every worker record, and the exclusive prefix
@@ -54,6 +57,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
   __shared__ int buf[PLAN_WAVES];
   __shared__ int32_t s_prefix[PLAN_LDS_SEQS + 1];
   __shared__ int32_t s_len[PLAN_LDS_SEQS];
+  __shared__ int32_t s_pcs[PLAN_LDS_SEQS];       // pieces of each sequence
+  __shared__ int32_t s_own[PLAN_LDS_WORKERS];    // sequence where a worker's range starts
   const int tid = threadIdx.x;
   int32_t* prefix = sched::unit_prefix(meta, W);
   const bool in_lds = B <= PLAN_LDS_SEQS;
@@ -86,7 +91,12 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
   int carry = 0;
   for (int base = 0; base < B; base += PLAN_THREADS) {
     const int b = base + tid;
-    const int v = b < B ? sched::seq_units(len[b], fix, T, W) : 0;
+    int v = 0;
+    if (b < B) {
+      const int n = sched::seq_pieces(len[b], fix, T, W);
+      v = sched::seq_pages(len[b]) + fix * n;  // seq_units
+      if (in_lds) s_pcs[b] = n;
+    }
     const int inc = block_scan(v, buf, &total);
     if (b < B) {
       prefix[b + 1] = carry + inc;
@@ -98,8 +108,44 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const int32_t* seqle
   __syncthreads();
   const int32_t* pre = in_lds ? s_prefix : prefix;
 
-  for (int w = tid; w < W; w += PLAN_THREADS)
-    sched::worker_record(w, W, pre, len, B, fix, T, sched::records(meta) + (size_t)w * sched::REC);
+  if (in_lds && W <= PLAN_LDS_WORKERS) {
+    // Each sequence marks the workers whose range starts among its units
+    // (the unit prefix rises strictly, so every worker start has exactly
+    // one owner); a worker's last sequence is the owner of its last unit,
+    // which the next worker's start gives. The same values as worker_record's
+    // binary searches, without their chains of dependent LDS reads.
+    const int32_t C = pre[B];
+    const int chunk = sched::chunk_units(C, W, fix);
+    for (int b = tid; b < B; b += PLAN_THREADS) {
+      const int w0 = (pre[b] + chunk - 1) / chunk;
+      const int w1 = min((pre[b + 1] + chunk - 1) / chunk, W);
+      for (int w = w0; w < w1; ++w) s_own[w] = b;
+    }
+    __syncthreads();
+    for (int w = tid; w < W; w += PLAN_THREADS) {
+      int32_t* rec = sched::records(meta) + (size_t)w * sched::REC;
+      const int64_t lo = (int64_t)w * chunk;
+      if (lo >= C) {
+        rec[sched::R_B_START] = 0; rec[sched::R_P_START] = 0; rec[sched::R_B_END] = -1;
+        rec[sched::R_P_END] = 0; rec[sched::R_SPLIT0] = 0; rec[sched::R_OWNS_FIRST] = 0;
+        rec[sched::R_LO] = C; rec[sched::R_HI] = C;
+        continue;
+      }
+      const int64_t hi = lo + chunk < C ? lo + chunk : C;
+      const int bs = s_own[w];
+      int be = B - 1;
+      if (hi < C) {  // worker w + 1 starts at hi
+        const int b1 = s_own[w + 1];
+        be = pre[b1] < hi ? b1 : b1 - 1;
+      }
+      sched::record_of(w, chunk, lo, hi, bs, be, sched::seq_pages(len[bs]), s_pcs[bs],
+                       sched::seq_pages(len[be]), s_pcs[be], pre, fix, rec);
+    }
+  } else {
+    for (int w = tid; w < W; w += PLAN_THREADS)
+      sched::worker_record(w, W, pre, len, B, fix, T,
+                           sched::records(meta) + (size_t)w * sched::REC);
+  }
 
   carry = 0;
   for (int base = 0; base < B; base += PLAN_THREADS) {

@@ -105,10 +105,8 @@ SCHED_HD int seq_units(int32_t L, int fix, int32_t T, int W) {
 // Pages of a sequence that lie before its unit offset x (0 <= x <= units):
 // the overhead units of a block count as lying before the block's pages.
 // (All in 32 bits: a sequence's units, like the whole line, fit in int32.)
-SCHED_HD int pages_before(int32_t L, int fix, int32_t T, int W, int32_t x) {
-  const int p = seq_pages(L);
-  if (p == 0) return 0;
-  const int n = seq_pieces(L, fix, T, W);
+// (with the sequence's pages p >= 1 and its pieces n = seq_pieces given)
+SCHED_HD int pages_before_pn(int p, int n, int fix, int32_t x) {
   const int q = p / n, r = p % n;  // blocks 0 .. r - 1 hold q + 1 pages, the rest q
   const int big = fix + q + 1, small = fix + q, xr = r * big;
   int i, off, before;
@@ -125,6 +123,11 @@ SCHED_HD int pages_before(int32_t L, int fix, int32_t T, int W, int32_t x) {
   const int bp = i < r ? q + 1 : q;
   const int in = off - fix;
   return before + (in < 0 ? 0 : (in > bp ? bp : in));
+}
+SCHED_HD int pages_before(int32_t L, int fix, int32_t T, int W, int32_t x) {
+  const int p = seq_pages(L);
+  if (p == 0) return 0;
+  return pages_before_pn(p, seq_pieces(L, fix, T, W), fix, x);
 }
 
 // Largest b in [0, B) with prefix[b] <= u (prefix strictly increasing,
@@ -145,6 +148,26 @@ SCHED_HD int chunk_units(int32_t total_units, int W, int fix) {
   return c > fix ? c : fix + 1;
 }
 
+// The rest of worker_record, with its first and last sequences bs and be
+// (the sequences holding unit offsets lo and hi - 1) already found.
+// pbs, nbs (pbe, nbe): pages and pieces (seq_pieces) of bs (be).
+SCHED_HD void record_of(int w, int chunk, int64_t lo, int64_t hi, int bs, int be, int pbs, int nbs,
+                        int pbe, int nbe, const int32_t* prefix, int fix, int32_t* rec) {
+  const int ps = pbs == 0 ? 0 : pages_before_pn(pbs, nbs, fix, (int32_t)(lo - prefix[bs]));
+  const int pe = pbe == 0 ? 0 : pages_before_pn(pbe, nbe, fix, (int32_t)(hi - prefix[be]));
+  // the worker holding the sequence's first page (its first block opens
+  // with the overhead units)
+  const int first_w = (prefix[bs] + fix) / chunk;
+  rec[R_B_START] = bs;
+  rec[R_P_START] = ps;
+  rec[R_B_END] = be;
+  rec[R_P_END] = pe;
+  rec[R_SPLIT0] = w > first_w ? w - first_w : 0;
+  rec[R_OWNS_FIRST] = prefix[bs] == lo ? 1 : 0;
+  rec[R_LO] = (int32_t)lo;
+  rec[R_HI] = (int32_t)hi;
+}
+
 // Record of worker w. prefix has B + 1 entries (prefix[B] = total units of
 // the line); T is the batch's cost from step 1.
 SCHED_HD void worker_record(int w, int W, const int32_t* prefix, const int32_t* seqlens,
@@ -160,19 +183,8 @@ SCHED_HD void worker_record(int w, int W, const int32_t* prefix, const int32_t* 
   const int64_t hi = (lo + chunk < C) ? lo + chunk : C;
   const int bs = find_seq(prefix, B, lo);
   const int be = find_seq(prefix, B, hi - 1);
-  const int ps = pages_before(seqlens[bs], fix, T, W, (int32_t)(lo - prefix[bs]));
-  const int pe = pages_before(seqlens[be], fix, T, W, (int32_t)(hi - prefix[be]));
-  // the worker holding the sequence's first page (its first block opens
-  // with the overhead units)
-  const int first_w = (prefix[bs] + fix) / chunk;
-  rec[R_B_START] = bs;
-  rec[R_P_START] = ps;
-  rec[R_B_END] = be;
-  rec[R_P_END] = pe;
-  rec[R_SPLIT0] = w > first_w ? w - first_w : 0;
-  rec[R_OWNS_FIRST] = prefix[bs] == lo ? 1 : 0;
-  rec[R_LO] = (int32_t)lo;
-  rec[R_HI] = (int32_t)hi;
+  record_of(w, chunk, lo, hi, bs, be, seq_pages(seqlens[bs]), seq_pieces(seqlens[bs], fix, T, W),
+            seq_pages(seqlens[be]), seq_pieces(seqlens[be], fix, T, W), prefix, fix, rec);
 }
 
 // Pages [p0, p1) of sequence b (with npg pages) that worker record rec

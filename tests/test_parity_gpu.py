@@ -191,7 +191,10 @@ def test_device_plan_equals_host_plan(dev):
                             # more sequences than the plan kernel's 1024 threads: the scans
                             # carry across blocks of the batch
                             (tuple(np.random.default_rng(5).integers(0, 3000, 2500)), 1, 16, 1, 512),
-                            (tuple([0] * 1500 + [1] * 700 + [64] * 30), 2, 128, 1, 512)]:
+                            (tuple([0] * 1500 + [1] * 700 + [64] * 30), 2, 128, 1, 512),
+                            # equal lengths (pieces on block boundaries) and one sequence
+                            # spread over every worker
+                            ((4096,) * 64, 1, 128, 1, 512), ((1 << 20,), 1, 16, 1, 512)]:
         sl = torch.tensor(Ls, dtype=torch.int32, device=dev)
         plan = lib.mla_decode_plan(sl, T, H, G, dv)
         torch.cuda.synchronize()
